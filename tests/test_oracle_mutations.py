@@ -1,0 +1,130 @@
+"""Planted mistakes in the oracle must each fail at least one pin (CPU only).
+
+Each mutant replaces one oracle function with a plausible wrong version (a dropped term, a wrong
+sign, an off-by-one route, a double rounding, a swapped nibble, a transposed layout ...) and runs
+the pins that should catch it. The oracle itself is restored after every case.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe_finalize_ref as R
+from tests import test_oracle_pins as P
+from tests import test_oracle_quant_pins as Q
+
+_orig = {name: getattr(R, name) for name in
+         ("finalize_unrounded", "round_to_format", "residual_rmsnorm", "quant_nvfp4",
+          "sf_offset")}
+
+
+def _fin_no_rsf(rows, idx, scales, shared, rsf):
+    return _orig["finalize_unrounded"](rows, idx, scales, shared, 1.0)
+
+
+def _fin_shared_sign(rows, idx, scales, shared, rsf):
+    neg = None if shared is None else -np.asarray(shared, dtype=np.float64)
+    return _orig["finalize_unrounded"](rows, idx, scales, neg, rsf)
+
+
+def _fin_scale_shift(rows, idx, scales, shared, rsf):
+    sc = None if scales is None else np.roll(np.asarray(scales, dtype=np.float64), 1, axis=1)
+    return _orig["finalize_unrounded"](rows, idx, sc, shared, rsf)
+
+
+def _fin_rsf_on_shared(rows, idx, scales, shared, rsf):
+    out = _orig["finalize_unrounded"](rows, idx, scales, shared, rsf)
+    return out if shared is None else out + (rsf - 1.0) * np.asarray(shared, dtype=np.float64)
+
+
+def _round_via_f32(x, fmt):
+    x = np.asarray(x, dtype=np.float64)
+    if fmt.name in ("bf16", "fp16"):
+        x = x.astype(np.float32).astype(np.float64)   # rounds twice
+    return _orig["round_to_format"](x, fmt)
+
+
+def _round_ties_away(x, fmt):
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    _, E = np.frexp(a)
+    e = np.maximum(E - 1, fmt.emin)
+    q = np.ldexp(1.0, e - fmt.frac_bits)
+    r = np.floor(a / q + 0.5) * q
+    r = np.where(r > fmt.max_finite, np.inf if fmt.overflow == "inf" else fmt.max_finite, r)
+    return np.copysign(r, x)
+
+
+def _rms_eps_outside(s, residual, gamma, eps, act):
+    fmt = R.FORMATS[act]
+    Rr = _orig["round_to_format"](np.asarray(s, np.float64) + np.asarray(residual, np.float64),
+                                  fmt)
+    ms = np.mean(Rr * Rr, axis=-1, keepdims=True)
+    N = _orig["round_to_format"](Rr * np.asarray(gamma, np.float64) / (np.sqrt(ms) + eps), fmt)
+    return Rr, N
+
+
+def _rms_unrounded_input(s, residual, gamma, eps, act):
+    fmt = R.FORMATS[act]
+    raw = np.asarray(s, np.float64) + np.asarray(residual, np.float64)
+    Rr = _orig["round_to_format"](raw, fmt)
+    ms = np.sum(raw * raw, axis=-1, keepdims=True) / raw.shape[-1]
+    N = _orig["round_to_format"](raw * np.asarray(gamma, np.float64) /
+                                 np.sqrt(ms + float(np.float32(eps))), fmt)
+    return Rr, N
+
+
+def _nvfp4_nibbles_swapped(N, gs, layout=1):
+    packed, sf = _orig["quant_nvfp4"](N, gs, layout)
+    return ((packed >> 4) | (packed << 4)).astype(np.uint8), sf
+
+
+def _sf_offset_transposed(t, b, H, layout):
+    if layout == R.SF_LINEAR:
+        return _orig["sf_offset"](t, b, H, layout)
+    nb = H // 16
+    n_col_tiles = (nb + 3) // 4
+    r = t % 128
+    tile = (t // 128) * n_col_tiles + b // 4
+    return tile * 512 + (r // 32) * 16 + (r % 32) * 4 + (b % 4) if r < 32 else \
+        tile * 512 + (r % 32) * 16 + (r // 32) * 4 + (b % 4)
+
+
+MUTANTS = [
+    ("finalize_unrounded", _fin_no_rsf, [P.test_finalize_exact_bruteforce,
+                                         P.test_dyadic_fixture_closed_form]),
+    ("finalize_unrounded", _fin_shared_sign, [P.test_finalize_exact_bruteforce]),
+    ("finalize_unrounded", _fin_scale_shift, [P.test_finalize_exact_bruteforce,
+                                              P.test_route_order_invariance]),
+    ("finalize_unrounded", _fin_rsf_on_shared, [P.test_dyadic_fixture_closed_form]),
+    ("round_to_format", _round_via_f32, [P.test_round_matches_exact_bruteforce]),
+    ("round_to_format", _round_ties_away, [P.test_round_matches_exact_bruteforce]),
+    ("residual_rmsnorm", _rms_eps_outside, [P.test_rmsnorm_correctly_rounded_bruteforce,
+                                             P.test_rmsnorm_constant_row_closed_form]),
+    ("residual_rmsnorm", _rms_unrounded_input, [P.test_rmsnorm_correctly_rounded_bruteforce]),
+    ("quant_nvfp4", _nvfp4_nibbles_swapped, [Q.test_nvfp4_exact_bruteforce]),
+    ("sf_offset", _sf_offset_transposed, [Q.test_sf_layout_tile_structure]),
+]
+
+_ARGS = {
+    P.test_finalize_exact_bruteforce: [("bf16", 6), ("fp16", 3)],
+    P.test_round_matches_exact_bruteforce: [("bf16",), ("fp16",)],
+    P.test_rmsnorm_correctly_rounded_bruteforce: [("bf16",)],
+    Q.test_nvfp4_exact_bruteforce: [(R.SF_SWIZZLED_128x4,)],
+}
+
+
+@pytest.mark.parametrize("target,mutant,pins", MUTANTS,
+                         ids=[m[1].__name__ for m in MUTANTS])
+def test_planted_mistake_is_caught(monkeypatch, target, mutant, pins):
+    monkeypatch.setattr(R, target, mutant)
+    monkeypatch.setattr(oracle, target, mutant)
+    caught = False
+    for pin in pins:
+        for args in _ARGS.get(pin, [()]):
+            try:
+                pin(*args)
+            except AssertionError:
+                caught = True
+    assert caught, f"no pin caught the mutant {mutant.__name__}"

@@ -1,0 +1,138 @@
+"""Pins of the oracle's NVFP4 / FP8 quantization and scale-factor layout (CPU only)."""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import make_inputs
+from tests.exact_ref import frac, rne_exact
+
+
+def _norm_out(T, H, seed, act="bf16"):
+    inp = make_inputs(T, H, 8, seed=seed, act_dtype=act)
+    rows = inp.rows.double().numpy()
+    _, _, N = O.finalize_rmsnorm(rows, inp.idx.numpy(), inp.scales.double().numpy(),
+                                 inp.shared.double().numpy(), 2.5, inp.residual.double().numpy(),
+                                 inp.gamma.double().numpy(), 1e-6, act)
+    return N
+
+
+def _unpack(packed):
+    lo = packed & 0xF
+    hi = packed >> 4
+    out = np.empty((packed.shape[0], packed.shape[1] * 2), dtype=np.uint8)
+    out[:, 0::2], out[:, 1::2] = lo, hi
+    return out
+
+
+@pytest.mark.parametrize("layout", [O.SF_SWIZZLED_128x4, O.SF_LINEAR])
+def test_nvfp4_exact_bruteforce(layout):
+    # Exact rationals: sf = RNE_e4m3(gs * amax / 6), q = RNE_e2m1(x * gs / sf), saturating.
+    T, H = 3, 48
+    N = _norm_out(T, H, seed=31)
+    N[1, 5] = -N[1, 5]  # make sure both signs occur in a block
+    gs = O.nvfp4_global_scale(N)
+    packed, sfb = O.quant_nvfp4(N, gs, layout)
+    codes = _unpack(packed)
+    G = Fraction(float(np.float32(gs)))
+    for t in range(T):
+        for b in range(H // 16):
+            blk = [frac(v) for v in N[t, 16 * b:16 * b + 16]]
+            amax = max(abs(v) for v in blk)
+            sf = rne_exact(G * amax / 6, "e4m3")
+            got_sf = O.decode_bits(np.uint8(sfb[O.sf_offset(t, b, H, layout)]), O.E4M3)
+            assert frac(got_sf) == sf
+            for i, v in enumerate(blk):
+                want = Fraction(0) if sf == 0 else rne_exact(v * G / sf, "e2m1")
+                c = codes[t, 16 * b + i]
+                assert frac(O.decode_bits(np.uint8(c), O.E2M1)) == want
+                if want == 0:
+                    assert (c >> 3) == (1 if v < 0 or (v == 0 and np.signbit(float(v))) else 0)
+
+
+def test_nvfp4_tensor_amax_block_gets_scale_448_and_code_6():
+    N = _norm_out(4, 256, seed=32)
+    gs = O.nvfp4_global_scale(N)
+    packed, sfb = O.quant_nvfp4(N, gs)
+    t, h = np.unravel_index(np.argmax(np.abs(N)), N.shape)
+    b = h // 16
+    sf = O.decode_bits(np.uint8(sfb[O.sf_offset(t, b, 256, O.SF_SWIZZLED_128x4)]), O.E4M3)
+    assert sf == 448.0
+    q = O.decode_bits(_unpack(packed)[t, h], O.E2M1)
+    assert abs(q) == 6.0 and np.sign(q) == np.sign(N[t, h])
+
+
+E2M1_VALUES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_nvfp4_dequant_error_bound():
+    # x * gs / sf lies between the midpoints around its code q (above 6 it saturates to 6).
+    N = _norm_out(5, 512, seed=33)
+    gs = O.nvfp4_global_scale(N)
+    packed, sfb = O.quant_nvfp4(N, gs)
+    codes = _unpack(packed)
+    q = O.decode_bits(codes, O.E2M1)
+    for t in range(5):
+        for b in range(512 // 16):
+            sf = float(O.decode_bits(np.uint8(sfb[O.sf_offset(t, b, 512, 1)]), O.E4M3))
+            for i in range(16):
+                x = N[t, 16 * b + i] * float(np.float32(gs)) / sf if sf else 0.0
+                qq = abs(q[t, 16 * b + i])
+                j = E2M1_VALUES.index(qq)
+                lo = (E2M1_VALUES[j - 1] + qq) / 2 if j else 0.0
+                hi = (E2M1_VALUES[j + 1] + qq) / 2 if qq < 6.0 else np.inf
+                assert lo <= abs(x) <= hi
+
+
+def test_sf_layout_size_bijection_padding():
+    for T, H in [(1, 64), (5, 48), (130, 96), (64, 6144), (128, 7168)]:
+        nb = H // 16
+        size = O.sf_size(T, H, O.SF_SWIZZLED_128x4)
+        assert size == ((T + 127) // 128 * 128) * ((nb + 3) // 4 * 4)
+        offs = {O.sf_offset(t, b, H, O.SF_SWIZZLED_128x4) for t in range(T) for b in range(nb)}
+        assert len(offs) == T * nb and min(offs) >= 0 and max(offs) < size
+        if T % 128:
+            # The lesson of the pages: a buffer of T*H/16 bytes is too small for this layout.
+            assert size > T * H // 16
+        lin = {O.sf_offset(t, b, H, O.SF_LINEAR) for t in range(T) for b in range(nb)}
+        assert lin == set(range(O.sf_size(T, H, O.SF_LINEAR)))
+    # Padding bytes of the swizzled buffer are zero.
+    N = _norm_out(5, 48, seed=34)
+    _, sfb = O.quant_nvfp4(N, O.nvfp4_global_scale(N))
+    used = {O.sf_offset(t, b, 48, 1) for t in range(5) for b in range(3)}
+    pad = [i for i in range(len(sfb)) if i not in used]
+    assert len(pad) == len(sfb) - 15 and not np.any(sfb[pad])
+    assert np.all(sfb[sorted(used)] != 0)
+
+
+def test_sf_layout_tile_structure():
+    # Within one 128-row x 4-block tile of 512 bytes, 4 consecutive blocks of a row are 4
+    # consecutive bytes, and rows r, r+32, r+64, r+96 share one 16-byte line. Tiles of the same
+    # row band follow each other along the blocks. (Parity of this byte map against an outside
+    # producer is unpinned: the pages name the layout but never print it.)
+    H = 16 * 12
+    for t in range(128):
+        base = O.sf_offset(t, 0, H, 1)
+        assert [O.sf_offset(t, b, H, 1) - base for b in range(4)] == [0, 1, 2, 3]
+        assert O.sf_offset(t, 4, H, 1) == base + 512
+        assert base // 16 == O.sf_offset(t % 32, 0, H, 1) // 16
+    assert O.sf_offset(128, 0, H, 1) == 3 * 512
+
+
+def test_fp8_exact_bruteforce_and_saturation():
+    N = _norm_out(2, 64, seed=35)
+    s8 = O.fp8_scale(N)
+    codes = O.quant_fp8(N, s8)
+    S = Fraction(float(np.float32(s8)))
+    for t in range(2):
+        for h in range(64):
+            want = rne_exact(frac(N[t, h]) * S, "e4m3")
+            assert frac(O.decode_bits(codes[t, h], O.E4M3)) == want
+    # saturation, signed zero
+    c = O.quant_fp8(np.array([[1000.0, -1000.0, -1e-30, 0.0]]), 1.0)
+    assert list(c[0]) == [0x7E, 0xFE, 0x80, 0x00]
+    # the tensor amax maps to 448
+    assert np.max(np.abs(O.decode_bits(codes, O.E4M3))) == 448.0
