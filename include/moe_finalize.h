@@ -1,0 +1,208 @@
+/*
+ * moe_finalize.h -- C ABI of the MI355X (gfx950) MoE finalize library, libmoe_finalize.so.
+ *
+ * Sources (cited by key):
+ *   [FI6631]  flashinfer PR #6631, "perf(comm): gather MoE-finalize routes together and accumulate
+ *             in FP32": Description, test changes, benchmark script, review walkthrough.
+ *   [TR16778] TensorRT-LLM PR #16778, "MoE: fp32 accumulation in deferred MoEAllReduce finalize":
+ *             Description / Fix.
+ *   [FI6546]  flashinfer PR #6546, small-batch trtllm-gen MoE finalize: Description.
+ *   [FI3385]  flashinfer PR #3385, "feat: MNNVL Allreduce quant fusion and performance
+ *             optimization": walkthrough and review comments.
+ *
+ * What is computed, for token t < T and hidden element h < H ([FI6631] Description and the FP64
+ * reference of its benchmark script; [TR16778] Fix):
+ *   route k of token t is present iff 0 <= p = expanded_idx_to_permuted_idx[t*K + k] < N_rows;
+ *   acc  = sum over present k of w[t,k] * X[p, h]        (float32 accumulation)
+ *   s    = RNE_T(RSF * acc + shared[t, h])               (the one rounding to the activation dtype)
+ *   r    = RNE_T(s + residual[t, h])                     (residual_out)
+ *   norm = RNE_T(r * gamma[h] / sqrt(mean_h(r^2) + eps))  (norm_out; RMSNorm of the rounded r)
+ * optionally followed by NVFP4 or FP8-E4M3 quantization of norm ([FI3385] walkthrough).
+ *
+ * Conventions shared by every entry point:
+ *   - Memory. Every array argument is caller-owned DEVICE memory on the current HIP device,
+ *     row-major and dense (leading dimension = the row length given). The library allocates
+ *     nothing per call and keeps no pointer after it returns.
+ *   - Streams. `stream` is a hipStream_t (NULL = the default stream). Calls only enqueue work and
+ *     return; they never synchronize, so they can be captured into a HIP graph.
+ *   - dtypes. act_dtype is MOE_DTYPE_BF16 or MOE_DTYPE_FP16 and types X, shared, residual,
+ *     gamma and every activation output. scales_dtype is MOE_DTYPE_FP32 or MOE_DTYPE_BF16.
+ *   - Optional inputs. expert_scales == NULL means weight 1.0; shared_expert_output == NULL means
+ *     no shared term; routed_scaling_factor 1.0 means "off" ([FI6631] review summary and commit
+ *     notes: missing scales handled, the factor is 1.0 when off).
+ *   - Absent routes. Any index outside [0, num_permuted_rows) (-1 marks "no route",
+ *     [FI6631] test changes) contributes nothing; neither its row nor its scale is read. An index
+ *     is never an error and never faults.
+ *   - Alignment. X, shared, residual, gamma and every output must be 16-byte aligned
+ *     (128-bit loads, [FI6546] Description; the vector-width guard of [FI3385] review), idx and
+ *     fp32 scales 4-byte, bf16 scales 2-byte. hidden must be a multiple of 8 (16 for NVFP4).
+ *   - Limits. 1 <= top_k <= 64 ([FI6546] Description: the small-batch rule admits topK <= 64);
+ *     num_tokens >= 0 (0 is a successful no-op); num_permuted_rows >= 0.
+ *   - Aliasing. Outputs may not overlap inputs or each other, except residual_out == residual
+ *     (exactly the same pointer) for an in-place residual update.
+ *   - Errors. 0 on success, a negative MOE_FIN_ERR_* code otherwise. Nothing is enqueued when a
+ *     check fails. No exception or abort crosses the ABI. moe_finalize_error_string() names a code.
+ *   - Determinism. Results are bitwise reproducible run to run and under graph capture/replay.
+ *   - Workspace (RMSNorm entry points). With workspace == NULL each token's row is handled by one
+ *     workgroup. With a workspace, a row may be spread over several workgroups that exchange
+ *     their partial sums of squares through it (summed in a fixed slice order, so results do
+ *     not depend on timing; the sum of squares is associated differently from the whole-row
+ *     kernel, so norm_out may differ from the NULL-workspace result in the last bit). It is
+ *     caller-owned device memory of at least moe_finalize_workspace_size(...) bytes, 256-byte
+ *     aligned, ZERO-FILLED ONCE before its first use; every call leaves it ready for the next
+ *     (no per-call clearing, so graph replays need no memset node). Calls that may run at the
+ *     same time (different streams) must use different workspaces. Its first 32-bit word is a
+ *     sticky flag that a kernel sets to nonzero if a workgroup gave up waiting for the other
+ *     slices of its row (outputs of that call are then unreliable); it stays 0 in normal use.
+ */
+#ifndef MOE_FINALIZE_H_
+#define MOE_FINALIZE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define MOE_FIN_OK 0
+#define MOE_FIN_ERR_NULL_POINTER (-1)   /* a required pointer is NULL                      */
+#define MOE_FIN_ERR_BAD_SHAPE (-2)      /* negative count, or a size that overflows         */
+#define MOE_FIN_ERR_BAD_TOPK (-3)       /* top_k outside [1, 64]                            */
+#define MOE_FIN_ERR_HIDDEN (-4)         /* hidden <= 0, not a multiple of 8 (16 for NVFP4)  */
+#define MOE_FIN_ERR_ALIGNMENT (-5)      /* a pointer is not aligned as required             */
+#define MOE_FIN_ERR_DTYPE (-6)          /* unknown act_dtype / scales_dtype                 */
+#define MOE_FIN_ERR_QUANT_TYPE (-7)     /* unknown quant_type                               */
+#define MOE_FIN_ERR_SF_LAYOUT (-8)      /* scale layout not LINEAR or SWIZZLED_128x4        */
+#define MOE_FIN_ERR_ALIAS (-9)          /* forbidden overlap between buffers                */
+#define MOE_FIN_ERR_HIP (-10)           /* the HIP runtime refused the launch               */
+#define MOE_FIN_ERR_WORKSPACE (-11)     /* workspace smaller than moe_finalize_workspace_size */
+
+/* Element types. */
+#define MOE_DTYPE_BF16 0
+#define MOE_DTYPE_FP16 1
+#define MOE_DTYPE_FP32 2
+
+/* Quantized output of moe_finalize_quant_run ([FI3385] walkthrough: FP8 and NVFP4 outputs). */
+#define MOE_QUANT_NVFP4 1
+#define MOE_QUANT_FP8_E4M3 2
+
+/* NVFP4 block-scale layouts ([FI3385] review: only LINEAR and SWIZZLED_128x4 are accepted). */
+#define MOE_SF_LINEAR 0
+#define MOE_SF_SWIZZLED_128x4 1
+
+/*
+ * moe_finalize_run -- the finalize alone (gather, float32 weighted sum, routed scaling, shared
+ * add, one rounding): out[t, h] = s as defined above. This is the op of [FI6546] Description
+ * (the trtllm-gen finalize) with the float32 accumulation of [FI6631] / [TR16778].
+ *
+ *   permuted_rows         [num_permuted_rows, hidden] act_dtype: expert GEMM2 output rows.
+ *   expanded_idx_to_permuted_idx [num_tokens, top_k] int32: entry (t, k) is the permuted row of
+ *                          expanded index t*top_k + k; out of range (e.g. -1) = no route.
+ *   expert_scales         [num_tokens, top_k] scales_dtype, or NULL (weight 1.0).
+ *   shared_expert_output  [num_tokens, hidden] act_dtype, or NULL.
+ *   out                   [num_tokens, hidden] act_dtype.
+ */
+int moe_finalize_run(const void* permuted_rows, int64_t num_permuted_rows,
+                     const int32_t* expanded_idx_to_permuted_idx,
+                     const void* expert_scales, int scales_dtype,
+                     const void* shared_expert_output, float routed_scaling_factor,
+                     void* out,
+                     int64_t num_tokens, int64_t hidden, int top_k, int act_dtype,
+                     void* stream);
+
+/*
+ * moe_finalize_rmsnorm_run -- finalize, then residual add and RMSNorm on the rounded sum
+ * ([FI6631] Description: the residual add and RMSNorm work on the rounded sum; its benchmark
+ * script: mean of squares over hidden, eps inside the square root, then times gamma).
+ *
+ *   residual      [num_tokens, hidden] act_dtype.
+ *   gamma         [hidden] act_dtype (RMSNorm weight).
+ *   eps           added to the mean of squares inside the square root.
+ *   residual_out  [num_tokens, hidden] act_dtype, or NULL (not written); may equal `residual`.
+ *   norm_out      [num_tokens, hidden] act_dtype.
+ *   workspace, workspace_bytes  see "Workspace" above (NULL, 0 allowed).
+ * Other arguments as in moe_finalize_run.
+ */
+int moe_finalize_rmsnorm_run(const void* permuted_rows, int64_t num_permuted_rows,
+                             const int32_t* expanded_idx_to_permuted_idx,
+                             const void* expert_scales, int scales_dtype,
+                             const void* shared_expert_output, float routed_scaling_factor,
+                             const void* residual, const void* gamma, float eps,
+                             void* residual_out, void* norm_out,
+                             void* workspace, size_t workspace_bytes,
+                             int64_t num_tokens, int64_t hidden, int top_k, int act_dtype,
+                             void* stream);
+
+/*
+ * moe_finalize_quant_run -- moe_finalize_rmsnorm_run followed by quantization of norm
+ * ([FI3385] walkthrough: FP8 / NVFP4 quantized outputs with an output scale and a layout code;
+ * [FI6631] test changes: the NVFP4 scale buffer is sized for SWIZZLED_128x4).
+ *
+ *   quant_type   MOE_QUANT_NVFP4 or MOE_QUANT_FP8_E4M3.
+ *   quant_scale  device pointer to ONE float32: the per-tensor global scale gs (NVFP4) or the
+ *                FP8 scale s8. NVFP4: for every 16-element block of a row, sf = E4M3(gs*amax/6)
+ *                and codes q = E2M1(x*gs/sf) (signed zeros when sf == 0). FP8: q = E4M3(x*s8).
+ *                All conversions round to nearest even and saturate (E4M3 at 448, E2M1 at 6);
+ *                the rounding decisions are exact (made in float64, where x*gs is exact).
+ *   quant_out    NVFP4: [num_tokens, hidden/2] bytes, element 2j in the low nibble of byte j.
+ *                FP8:   [num_tokens, hidden] bytes.
+ *   scale_out    NVFP4 only (else ignored, may be NULL): moe_finalize_sf_size(...) bytes of E4M3
+ *                block scales in `sf_layout`; every padding byte is written as 0.
+ *   sf_layout    MOE_SF_SWIZZLED_128x4 or MOE_SF_LINEAR (NVFP4 only).
+ *   residual_out as in moe_finalize_rmsnorm_run (nullable).
+ *   norm_out     [num_tokens, hidden] act_dtype, or NULL (then the unquantized norm is not stored).
+ *   workspace, workspace_bytes  see "Workspace" above (NULL, 0 allowed).
+ * Other arguments as in moe_finalize_rmsnorm_run.
+ */
+int moe_finalize_quant_run(const void* permuted_rows, int64_t num_permuted_rows,
+                           const int32_t* expanded_idx_to_permuted_idx,
+                           const void* expert_scales, int scales_dtype,
+                           const void* shared_expert_output, float routed_scaling_factor,
+                           const void* residual, const void* gamma, float eps,
+                           int quant_type, const float* quant_scale,
+                           void* quant_out, void* scale_out, int sf_layout,
+                           void* residual_out, void* norm_out,
+                           void* workspace, size_t workspace_bytes,
+                           int64_t num_tokens, int64_t hidden, int top_k, int act_dtype,
+                           void* stream);
+
+/*
+ * moe_finalize_workspace_size -- bytes of workspace the RMSNorm entry points may use for a call
+ * with this shape (256 + 512 per token). Host-only. Returns 0 for num_tokens < 0.
+ */
+size_t moe_finalize_workspace_size(int64_t num_tokens, int64_t hidden, int top_k);
+
+/*
+ * moe_finalize_sf_size -- bytes of the NVFP4 block-scale buffer for a [num_tokens, hidden]
+ * output: SWIZZLED_128x4 pads rows to a multiple of 128 and blocks per row to a multiple of 4,
+ * roundup(T,128) * roundup(H/16,4) ([FI6631] test changes: T*H/16 bytes is too small and was
+ * overrun); LINEAR is T * H/16. Returns 0 for an unknown layout or a negative size.
+ * Host-only, never touches the GPU.
+ */
+size_t moe_finalize_sf_size(int64_t num_tokens, int64_t hidden, int sf_layout);
+
+/*
+ * moe_finalize_launch_floor_run -- measurement aid: enqueue an EMPTY kernel with exactly the grid,
+ * block and LDS size that entry point `entry` (0 = moe_finalize_run, 1 = moe_finalize_rmsnorm_run,
+ * 2 = moe_finalize_quant_run, the RMSNorm ones with a workspace) would use for this shape. Its
+ * time per launch is the launch-latency
+ * floor the small-batch (T <= 16) timings are reported against. Reads and writes no memory.
+ * Returns the validation codes of the entry point for bad shapes (an unknown `entry` gives
+ * MOE_FIN_ERR_QUANT_TYPE).
+ */
+int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden, int top_k,
+                                  void* stream);
+
+/* Static, NUL-terminated description of a return code. Host-only. */
+const char* moe_finalize_error_string(int code);
+
+/* Library version (major*10000 + minor*100 + patch). Host-only. */
+int moe_finalize_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FINALIZE_H_ */

@@ -1,0 +1,174 @@
+"""Thin ctypes binding of libmoe_finalize.so (argument marshalling only).
+
+Every function here has the name of the C entry point it calls and does nothing but pass
+pointers, sizes, dtype codes and the current HIP stream of the tensors' device. All arithmetic
+runs in the library's HIP kernels. If the library is not built, importing this module fails
+loudly; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+from .build_lib import LIB_PATH
+
+MOE_DTYPE_BF16, MOE_DTYPE_FP16, MOE_DTYPE_FP32 = 0, 1, 2
+MOE_QUANT_NVFP4, MOE_QUANT_FP8_E4M3 = 1, 2
+MOE_SF_LINEAR, MOE_SF_SWIZZLED_128x4 = 0, 1
+
+# Every symbol include/moe_finalize.h declares.
+EXPORTED = ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_run",
+            "moe_finalize_sf_size", "moe_finalize_error_string", "moe_finalize_version",
+            "moe_finalize_launch_floor_run", "moe_finalize_workspace_size")
+
+_ACT = {torch.bfloat16: MOE_DTYPE_BF16, torch.float16: MOE_DTYPE_FP16}
+_SCALE = {torch.float32: MOE_DTYPE_FP32, torch.bfloat16: MOE_DTYPE_BF16}
+
+
+class MoeFinalizeError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{msg} (code {code})")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python moe_expert_output_amd/build_lib.py` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    lib.moe_finalize_run.argtypes = [vp, i64, vp, vp, i32, vp, f32, vp, i64, i64, i32, i32, vp]
+    sz = ctypes.c_size_t
+    lib.moe_finalize_rmsnorm_run.argtypes = [vp, i64, vp, vp, i32, vp, f32, vp, vp, f32, vp, vp,
+                                             vp, sz, i64, i64, i32, i32, vp]
+    lib.moe_finalize_quant_run.argtypes = [vp, i64, vp, vp, i32, vp, f32, vp, vp, f32, i32, vp,
+                                           vp, vp, i32, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.moe_finalize_workspace_size.argtypes = [i64, i64, i32]
+    lib.moe_finalize_workspace_size.restype = sz
+    for f in ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_run"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.moe_finalize_sf_size.argtypes = [i64, i64, i32]
+    lib.moe_finalize_sf_size.restype = ctypes.c_size_t
+    lib.moe_finalize_error_string.argtypes = [i32]
+    lib.moe_finalize_error_string.restype = ctypes.c_char_p
+    lib.moe_finalize_version.restype = ctypes.c_int
+    lib.moe_finalize_launch_floor_run.argtypes = [i32, i64, i64, i32, vp]
+    lib.moe_finalize_launch_floor_run.restype = ctypes.c_int
+    return lib
+
+
+LIB = _load()
+
+
+def moe_finalize_error_string(code: int) -> str:
+    return LIB.moe_finalize_error_string(int(code)).decode()
+
+
+def moe_finalize_sf_size(num_tokens: int, hidden: int, sf_layout: int) -> int:
+    return int(LIB.moe_finalize_sf_size(int(num_tokens), int(hidden), int(sf_layout)))
+
+
+def moe_finalize_workspace_size(num_tokens: int, hidden: int, top_k: int) -> int:
+    return int(LIB.moe_finalize_workspace_size(int(num_tokens), int(hidden), int(top_k)))
+
+
+def _ws(workspace: Optional[torch.Tensor]):
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def moe_finalize_version() -> int:
+    return int(LIB.moe_finalize_version())
+
+
+def moe_finalize_launch_floor_run(entry: int, num_tokens: int, hidden: int, top_k: int,
+                                  device=None, stream=None) -> None:
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    s = int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream) if stream is not None \
+        else torch.cuda.current_stream(dev).cuda_stream
+    _check(LIB.moe_finalize_launch_floor_run(int(entry), int(num_tokens), int(hidden), int(top_k),
+                                             s))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be device (HIP) tensors")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() or None
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise MoeFinalizeError(code, moe_finalize_error_string(code))
+
+
+def _stream(ref: torch.Tensor, stream) -> int:
+    if stream is not None:
+        return int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    return torch.cuda.current_stream(ref.device).cuda_stream
+
+
+def _common(rows, idx, scales):
+    if rows.dtype not in _ACT:
+        raise ValueError(f"activation dtype {rows.dtype} is not bf16/fp16")
+    sdt = _SCALE.get(scales.dtype, -1) if scales is not None else MOE_DTYPE_FP32
+    T, K = idx.shape
+    return _ACT[rows.dtype], sdt, T, K
+
+
+def moe_finalize_run(permuted_rows: torch.Tensor, expanded_idx_to_permuted_idx: torch.Tensor,
+                     expert_scales: Optional[torch.Tensor],
+                     shared_expert_output: Optional[torch.Tensor],
+                     routed_scaling_factor: float, out: torch.Tensor, stream=None) -> None:
+    act, sdt, T, K = _common(permuted_rows, expanded_idx_to_permuted_idx, expert_scales)
+    H = out.shape[-1]
+    _check(LIB.moe_finalize_run(
+        _ptr(permuted_rows), permuted_rows.shape[0], _ptr(expanded_idx_to_permuted_idx),
+        _ptr(expert_scales), sdt, _ptr(shared_expert_output), float(routed_scaling_factor),
+        _ptr(out), T, H, K, act, _stream(out, stream)))
+
+
+def moe_finalize_rmsnorm_run(permuted_rows: torch.Tensor,
+                             expanded_idx_to_permuted_idx: torch.Tensor,
+                             expert_scales: Optional[torch.Tensor],
+                             shared_expert_output: Optional[torch.Tensor],
+                             routed_scaling_factor: float, residual: torch.Tensor,
+                             gamma: torch.Tensor, eps: float,
+                             residual_out: Optional[torch.Tensor], norm_out: torch.Tensor,
+                             workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    act, sdt, T, K = _common(permuted_rows, expanded_idx_to_permuted_idx, expert_scales)
+    H = residual.shape[-1]
+    wp, wb = _ws(workspace)
+    _check(LIB.moe_finalize_rmsnorm_run(
+        _ptr(permuted_rows), permuted_rows.shape[0], _ptr(expanded_idx_to_permuted_idx),
+        _ptr(expert_scales), sdt, _ptr(shared_expert_output), float(routed_scaling_factor),
+        _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out), _ptr(norm_out), wp, wb,
+        T, H, K, act, _stream(residual, stream)))
+
+
+def moe_finalize_quant_run(permuted_rows: torch.Tensor, expanded_idx_to_permuted_idx: torch.Tensor,
+                           expert_scales: Optional[torch.Tensor],
+                           shared_expert_output: Optional[torch.Tensor],
+                           routed_scaling_factor: float, residual: torch.Tensor,
+                           gamma: torch.Tensor, eps: float, quant_type: int,
+                           quant_scale: torch.Tensor, quant_out: torch.Tensor,
+                           scale_out: Optional[torch.Tensor], sf_layout: int,
+                           residual_out: Optional[torch.Tensor], norm_out: Optional[torch.Tensor],
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    act, sdt, T, K = _common(permuted_rows, expanded_idx_to_permuted_idx, expert_scales)
+    H = residual.shape[-1]
+    wp, wb = _ws(workspace)
+    _check(LIB.moe_finalize_quant_run(
+        _ptr(permuted_rows), permuted_rows.shape[0], _ptr(expanded_idx_to_permuted_idx),
+        _ptr(expert_scales), sdt, _ptr(shared_expert_output), float(routed_scaling_factor),
+        _ptr(residual), _ptr(gamma), float(eps), int(quant_type), _ptr(quant_scale),
+        _ptr(quant_out), _ptr(scale_out), int(sf_layout), _ptr(residual_out), _ptr(norm_out),
+        wp, wb, T, H, K, act, _stream(residual, stream)))

@@ -1,0 +1,137 @@
+// device_utils.h -- gfx950 device helpers of the MoE finalize kernels: 128-bit activation
+// packing, wavefront reductions over DPP, and exact-decision FP8/FP4 encoders.
+//
+// Sources (cited by key): [FI6631] flashinfer PR #6631 "perf(comm): gather MoE-finalize routes
+// together and accumulate in FP32"; [FI3385] flashinfer PR #3385 "feat: MNNVL Allreduce quant
+// fusion and performance optimization".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mfin {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+enum : int { ACT_BF16 = 0, ACT_FP16 = 1 };
+
+// --- activation packing: 8 elements of bf16/fp16 in one 128-bit word ---------------------------
+template <int ACT>
+struct Act;
+
+template <>
+struct Act<ACT_BF16> {
+  static __device__ __forceinline__ void unpack(const u32x4 v, float f[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __builtin_bit_cast(float, v[i] << 16);
+      f[2 * i + 1] = __builtin_bit_cast(float, v[i] & 0xFFFF0000u);
+    }
+  }
+  // Round-to-nearest-even float -> bf16 (v_cvt_pk_bf16_f32).
+  static __device__ __forceinline__ u32x4 pack(const float f[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f32x2 x = {f[2 * i], f[2 * i + 1]};
+      r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+    }
+    return r;
+  }
+  static __device__ __forceinline__ float scalar(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+  }
+};
+
+template <>
+struct Act<ACT_FP16> {
+  static __device__ __forceinline__ void unpack(const u32x4 v, float f[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // Copy the element out first: bit-casting a vector-element lvalue directly has been seen
+      // to read element 0 for every i.
+      const uint32_t word = v[i];
+      f32x2 x = __builtin_convertvector(__builtin_bit_cast(f16x2, word), f32x2);
+      f[2 * i] = x[0];
+      f[2 * i + 1] = x[1];
+    }
+  }
+  // Round-to-nearest-even float -> fp16 (default rounding mode; never the RTZ pack).
+  static __device__ __forceinline__ u32x4 pack(const float f[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f16x2 h;
+      h[0] = (_Float16)f[2 * i];
+      h[1] = (_Float16)f[2 * i + 1];
+      r[i] = __builtin_bit_cast(uint32_t, h);
+    }
+    return r;
+  }
+};
+
+// --- wavefront sum over DPP ---------------------------------------------------------------------
+// Sums v over the 64 lanes of a wavefront in a fixed order (so the result is bitwise
+// reproducible): quad swaps, half-row and row mirrors give every lane its 16-lane row sum, then
+// the four row sums (lanes 15, 31, 47, 63) are added in row order. Returns the sum in all lanes.
+#define MFIN_DPP_ADD(v, ctrl)                                                                   \
+  (v) += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(                                 \
+             0, __builtin_bit_cast(int, (v)), (ctrl), 0xF, 0xF, false))
+
+__device__ __forceinline__ float wave_sum(float v) {
+  MFIN_DPP_ADD(v, 0xB1);   // quad_perm [1,0,3,2]
+  MFIN_DPP_ADD(v, 0x4E);   // quad_perm [2,3,0,1]
+  MFIN_DPP_ADD(v, 0x141);  // row_half_mirror
+  MFIN_DPP_ADD(v, 0x140);  // row_mirror: every lane now holds its row (16 lanes) sum
+  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
+  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
+  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Maximum of v and the value of lane ^ 1 (the other half of a 16-element NVFP4 block).
+__device__ __forceinline__ float pair_max(float v) {
+  float o = __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  return fmaxf(v, o);
+}
+
+// --- exact-decision narrow encoders (inputs are exact FP64 magnitudes) -------------------------
+// OCP E4M3 ("fn"): bias 7, 3 mantissa bits, subnormals m * 2^-9, max 448. Round to nearest
+// even, saturate at 448. y >= 0, finite or NaN. Returns the 7-bit magnitude code.
+__device__ __forceinline__ uint32_t e4m3_code(double y) {
+  if (!(y == y)) return 0x7Fu;
+  if (y >= 448.0) return 0x7Eu;
+  if (y == 0.0) return 0u;
+  int e = __builtin_amdgcn_frexp_exp(y) - 1;  // y = m * 2^e, m in [1, 2)
+  e = e < -6 ? -6 : e;                        // below 2^-6 the spacing stays 2^-9 (subnormals)
+  double r = __builtin_rint(__builtin_amdgcn_ldexp(y, 3 - e));  // exact scale, RNE to integer
+  // normal: r in [8, 16]; subnormal: r in [0, 8]. A carry to 16 moves to the next binade.
+  return (uint32_t)((e + 7) * 8 + (int)r - 8);
+}
+
+__device__ __forceinline__ double e4m3_value(uint32_t c) {
+  uint32_t ex = (c >> 3) & 0xFu, m = c & 7u;
+  if (ex == 0) return __builtin_amdgcn_ldexp((double)m, -9);
+  return __builtin_amdgcn_ldexp((double)(8 + m), (int)ex - 10);
+}
+
+// E2M1 magnitude code of a*gs/sf given a_gs = |x| * gs (exact) and sf > 0: round to nearest
+// even among {0, .5, 1, 1.5, 2, 3, 4, 6} (codes 0..7), saturate at 6. Comparing a_gs against
+// midpoint*sf (exact products of narrow values) avoids any division.
+__device__ __forceinline__ uint32_t e2m1_code(double a_gs, double sf) {
+  // ties to the even code: midpoints 0.25, 1.25, 2.5, 5 go down; 0.75, 1.75, 3.5 go up.
+  return (uint32_t)(a_gs > 0.25 * sf) + (uint32_t)(a_gs >= 0.75 * sf) +
+         (uint32_t)(a_gs > 1.25 * sf) + (uint32_t)(a_gs >= 1.75 * sf) +
+         (uint32_t)(a_gs > 2.5 * sf) + (uint32_t)(a_gs >= 3.5 * sf) + (uint32_t)(a_gs > 5.0 * sf);
+}
+
+__device__ __forceinline__ uint32_t sign_bit(float x) {
+  return __builtin_bit_cast(uint32_t, x) >> 31;
+}
+
+}  // namespace mfin

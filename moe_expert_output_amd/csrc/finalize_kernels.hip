@@ -1,0 +1,812 @@
+// finalize_kernels.hip -- gfx950 kernels and C ABI of the MoE finalize library.
+//
+// Sources (cited by key):
+//   [FI6631]  flashinfer PR #6631, "perf(comm): gather MoE-finalize routes together and accumulate
+//             in FP32": Description (indices and scales of the routes loaded before their rows,
+//             float32 accumulation rounded once, residual add + RMSNorm on the rounded sum),
+//             test changes (-1 routes, top_k 6/8/10, swizzled scale buffer size).
+//   [TR16778] TensorRT-LLM PR #16778, "MoE: fp32 accumulation in deferred MoEAllReduce finalize":
+//             Fix (top-k sum and shared add in a float32 array, rounded once).
+//   [FI6546]  flashinfer PR #6546, small-batch trtllm-gen finalize: Description (one block per
+//             token and hidden slice, 128-bit loads, top-k split over thread groups combined in
+//             shared memory, top_k <= 64).
+//   [FI3385]  flashinfer PR #3385, "feat: MNNVL Allreduce quant fusion and performance
+//             optimization": walkthrough (FP8 / NVFP4 outputs, SF layouts), review comments
+//             (vector-width guard, layout whitelist, null-guarded optional outputs).
+//
+// Kernel design (gfx950, wave64). One workgroup handles one token and a contiguous range of
+// 8-element (16-byte) hidden slots; for the RMSNorm modes the range is the whole row so the sum
+// of squares stays inside the workgroup. The workgroup's lanes are split into G route groups of
+// L lanes (L a multiple of 64, so every wavefront belongs to one group); group g takes routes
+// g, g+G, g+2G, ... Every wavefront first loads all K indices and scales of its token in one
+// coalesced load (lane k holds route k) and reads them back with readlane, so row addresses are
+// wave-uniform; it then issues every present route's 128-bit row load (in chunks of at most 16
+// routes) before it consumes any of them, accumulates in float32, and hands its partials to group 0
+// through LDS, which adds them in group order (deterministic). Group 0 applies the routed
+// scaling and shared add, rounds once, adds the residual, and reduces the sum of squares with a
+// DPP wavefront reduction plus one LDS pass across wavefronts. Quantized outputs are encoded
+// with exact rounding decisions made in float64.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <initializer_list>
+
+#include "../../include/moe_finalize.h"
+#include "device_utils.h"
+
+namespace mfin {
+
+enum : int { MODE_FIN = 0, MODE_RMS = 1, MODE_NVFP4 = 2, MODE_FP8 = 3 };
+
+struct Params {
+  const uint8_t* rows;       // [n_rows, H] act dtype
+  int64_t n_rows;
+  const int32_t* idx;        // [T, K]
+  const void* scales;        // [T, K] fp32 or bf16, or null
+  int scales_bf16;
+  const uint8_t* shared;     // [T, H] or null
+  float rsf;
+  const uint8_t* residual;   // [T, H]
+  const uint8_t* gamma;      // [H]
+  float eps;
+  float inv_h;
+  uint8_t* out;              // MODE_FIN: finalize output; else norm_out (nullable in quant)
+  uint8_t* residual_out;     // nullable
+  uint8_t* quant_out;
+  uint8_t* sf_out;
+  const float* qscale;
+  int sf_swizzled;
+  int T, H, K;
+  int nv;                    // H / 8 slots per row
+  int lanes;                 // L: lanes per route group (multiple of 64)
+  int slot_span;             // slots covered by one workgroup (L * P)
+  int slices;                // workgroups per token (> 1: the row is split, see below)
+  uint8_t* ws;               // workspace of the split row modes (null when slices == 1)
+};
+
+// Split rows. When a token's row is spread over `slices` workgroups, each workgroup publishes
+// the sum of squares of its slice in the caller's workspace and waits for the other slices of
+// its token. Layout: a 256-byte header whose first word is a sticky timeout flag, then one
+// 512-byte block per token holding kMaxSlices 64-bit slots. A slot carries (epoch << 32 |
+// float bits of a partial) in ONE relaxed device-scope atomic word, so the flag and the data
+// become visible together and no release/acquire fences (L2 writeback / invalidate) are needed.
+// All kMaxSlices slots of a token hold the same epoch between calls: slice j rewrites every slot
+// m with m % slices == j, so a call reads the current epoch from its own slot and waits until
+// slots 0..slices-1 carry epoch + 1. A zero-filled workspace is valid, no call needs a reset, and
+// the slice count may change from call to call.
+constexpr int kMaxSlices = 64;
+constexpr size_t kWsHeader = 256, kWsPerToken = 8 * kMaxSlices;
+constexpr uint32_t kMaxSpins = 1u << 22;      // ~0.1-0.5 s of polling, then give up (flagged)
+
+// Partial sums of route groups g >= 1: [G-1][P][L] x 8 floats.
+extern __shared__ float4 lds_dyn[];
+
+template <int ACT, int MODE, int G, int P, int JMAX>
+__global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
+  // blockIdx.x = token * slices + slice (one slice per token in the row modes)
+  const int t = blockIdx.x / a.slices;
+  const int slice = blockIdx.x - t * a.slices;
+  const int tid = threadIdx.x;
+  const int L = a.lanes;
+  const int g = __builtin_amdgcn_readfirstlane(tid / L);   // wave-uniform route group
+  const int lane = tid - g * L;
+  const int slot0 = slice * a.slot_span;
+
+  // ---- route metadata: all K indices and scales of the token in one coalesced load per
+  // wavefront (lane k holds route k), issued before any row load. Routes are later read back
+  // with readlane, so their row addresses are wave-uniform (scalar base + lane offset).
+  const int lane64 = tid & 63;
+  int my_idx = -1;
+  float my_w = 0.f;
+  if (lane64 < a.K) {
+    const int64_t mk = (int64_t)t * a.K + lane64;
+    my_idx = a.idx[mk];
+    if (a.scales == nullptr) {
+      my_w = 1.f;
+    } else if (a.scales_bf16) {
+      my_w = Act<ACT_BF16>::scalar(((const uint16_t*)a.scales)[mk]);
+    } else {
+      my_w = ((const float*)a.scales)[mk];
+    }
+  }
+
+  // ---- this lane's slots ----
+  int slot[P];
+  bool live[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    slot[p] = slot0 + lane + p * L;
+    live[p] = slot[p] < a.nv && (lane + p * L) < a.slot_span;
+  }
+
+  const int64_t row_bytes = (int64_t)a.H * 2;
+
+  // Group 0 also needs the shared-expert, residual and gamma slices; issue them up front.
+  u32x4 shv[P], resv[P], gamv[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) shv[p] = resv[p] = gamv[p] = (u32x4){0u, 0u, 0u, 0u};
+  if (g == 0) {
+    const int64_t tok_off = (int64_t)t * row_bytes;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      if (live[p]) {
+        if (a.shared) shv[p] = ((const u32x4*)(a.shared + tok_off))[slot[p]];
+        if (MODE != MODE_FIN) {
+          resv[p] = ((const u32x4*)(a.residual + tok_off))[slot[p]];
+          gamv[p] = ((const u32x4*)a.gamma)[slot[p]];
+        }
+      }
+    }
+  }
+
+  // ---- row gather: per chunk of CH routes, issue every present route's 128-bit loads, then
+  // accumulate them in float32 (fused multiply-add) ----
+  constexpr int CH = JMAX < 16 / P ? JMAX : 16 / P;
+  float acc[P][8];
+#pragma unroll
+  for (int p = 0; p < P; ++p)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[p][e] = 0.f;
+#pragma unroll
+  for (int c0 = 0; c0 < JMAX; c0 += CH) {
+    if (g + c0 * G >= a.K) break;
+    int pidx[CH];
+    float w[CH];
+    bool present[CH];
+    u32x4 v[CH][P];
+#pragma unroll
+    for (int jj = 0; jj < CH; ++jj) {
+      const int k = g + (c0 + jj) * G;
+      const int kk = k < a.K ? k : 0;
+      pidx[jj] = __builtin_amdgcn_readlane(my_idx, kk);
+      w[jj] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), kk));
+      present[jj] = k < a.K && (uint64_t)(int64_t)pidx[jj] < (uint64_t)a.n_rows;
+      const u32x4* rowp = (const u32x4*)(a.rows + (int64_t)pidx[jj] * row_bytes);
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        v[jj][p] = (u32x4){0u, 0u, 0u, 0u};
+        if (present[jj] && live[p]) v[jj][p] = rowp[slot[p]];
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < CH; ++jj) {
+      if (!present[jj]) continue;
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        float x[8];
+        Act<ACT>::unpack(v[jj][p], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[p][e] = __builtin_fmaf(w[jj], x[e], acc[p][e]);
+      }
+    }
+  }
+
+  // ---- combine the route groups through LDS, in group order ----
+  if constexpr (G > 1) {
+    if (g > 0) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        float4* dst = lds_dyn + ((size_t)((g - 1) * P + p) * L + lane) * 2;
+        dst[0] = make_float4(acc[p][0], acc[p][1], acc[p][2], acc[p][3]);
+        dst[1] = make_float4(acc[p][4], acc[p][5], acc[p][6], acc[p][7]);
+      }
+    }
+    __syncthreads();
+    if (g == 0) {
+#pragma unroll
+      for (int gg = 1; gg < G; ++gg) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const float4* src = lds_dyn + ((size_t)((gg - 1) * P + p) * L + lane) * 2;
+          float4 u0 = src[0], u1 = src[1];
+          acc[p][0] += u0.x; acc[p][1] += u0.y; acc[p][2] += u0.z; acc[p][3] += u0.w;
+          acc[p][4] += u1.x; acc[p][5] += u1.y; acc[p][6] += u1.z; acc[p][7] += u1.w;
+        }
+      }
+    }
+  }
+
+  // ---- routed scaling, shared add, the one rounding; then residual add ----
+  float r[P][8];
+  float ss = 0.f;
+  if (g == 0) {
+    const int64_t tok_off = (int64_t)t * row_bytes;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      float sh[8];
+      Act<ACT>::unpack(shv[p], sh);
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sv[e] = __builtin_fmaf(a.rsf, acc[p][e], sh[e]);
+      const u32x4 s_pk = Act<ACT>::pack(sv);
+      if constexpr (MODE == MODE_FIN) {
+        if (live[p]) ((u32x4*)(a.out + tok_off))[slot[p]] = s_pk;
+      } else {
+        float s_r[8], res[8];
+        Act<ACT>::unpack(s_pk, s_r);
+        Act<ACT>::unpack(resv[p], res);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[p][e] = s_r[e] + res[e];
+        const u32x4 r_pk = Act<ACT>::pack(r[p]);
+        Act<ACT>::unpack(r_pk, r[p]);                 // keep the rounded residual_out
+        if (live[p]) {
+          if (a.residual_out) ((u32x4*)(a.residual_out + tok_off))[slot[p]] = r_pk;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(r[p][e], r[p][e], ss);
+        }
+      }
+    }
+  }
+  if constexpr (MODE == MODE_FIN) return;
+
+  // ---- RMSNorm: sum of squares over the row (DPP within wavefronts, one LDS pass across,
+  // then, for a split row, the slice partials of the token in slice order) ----
+  __shared__ float wave_part[16];
+  __shared__ float row_total;
+  const int wave = tid >> 6;
+  const int n_waves0 = L >> 6;                  // wavefronts of group 0
+  if (g == 0) {
+    const float ws = wave_sum(ss);
+    if ((tid & 63) == 0) wave_part[wave] = ws;
+  }
+  __syncthreads();
+  if (tid < 64) {                               // wavefront 0 of the workgroup
+    float tot = 0.f;
+    for (int i = 0; i < n_waves0; ++i) tot += wave_part[i];
+    if (a.slices > 1) {
+      uint64_t* slot = (uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken);
+      const int S = a.slices;
+      const uint32_t epoch =
+          (uint32_t)(__hip_atomic_load(slot + slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >>
+                     32) + 1u;
+      const int m = slice + tid * S;              // this slice's slots
+      if (m < kMaxSlices) {
+        const uint64_t v = ((uint64_t)epoch << 32) |
+                           (m == slice ? (uint64_t)__builtin_bit_cast(uint32_t, tot) : 0ull);
+        __hip_atomic_store(slot + m, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      // lane j < S waits for slice j's word of this epoch
+      uint32_t bits = 0;
+      if (tid < S) {
+        uint32_t spins = 0;
+        while (true) {
+          const uint64_t x = __hip_atomic_load(slot + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if ((uint32_t)(x >> 32) == epoch) {
+            bits = (uint32_t)x;
+            break;
+          }
+          if (++spins > kMaxSpins) {
+            __hip_atomic_fetch_or((uint32_t*)a.ws, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      tot = 0.f;
+      for (int j = 0; j < S; ++j)                 // slice order: deterministic
+        tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)bits, j));
+    }
+    if (tid == 0) row_total = tot;
+  }
+  __syncthreads();
+  if (g != 0) return;
+  const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(row_total, a.inv_h, a.eps));
+
+  const int64_t tok_off = (int64_t)t * row_bytes;
+  [[maybe_unused]] double qs = 0.0;
+  if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) qs = (double)*a.qscale;
+#pragma unroll
+  for (int p = 0; p < P; ++p) {
+    float gm[8], n[8];
+    Act<ACT>::unpack(gamv[p], gm);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) n[e] = (r[p][e] * rinv) * gm[e];
+    const u32x4 n_pk = Act<ACT>::pack(n);
+    if (a.out && live[p]) ((u32x4*)(a.out + tok_off))[slot[p]] = n_pk;
+    if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) {
+      float nr[8];
+      Act<ACT>::unpack(n_pk, nr);               // quantize the rounded norm_out values
+      if constexpr (MODE == MODE_FP8) {
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t c = e4m3_code(__builtin_fabs((double)nr[e]) * qs) | (sign_bit(nr[e]) << 7);
+          if (e < 4) lo |= c << (8 * e); else hi |= c << (8 * (e - 4));
+        }
+        if (live[p]) {
+          uint2* q = (uint2*)(a.quant_out + (int64_t)t * a.H) + slot[p];
+          *q = make_uint2(lo, hi);
+        }
+      } else {
+        // NVFP4: 16-element block = this lane's 8 elements + the neighbouring lane's 8.
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, __builtin_fabsf(nr[e]));
+        amax = pair_max(amax);
+        const uint32_t sfc = e4m3_code((double)amax * qs / 6.0);
+        const double sf = e4m3_value(sfc);
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t m = 0;
+          if (sfc != 0) m = e2m1_code(__builtin_fabs((double)nr[e]) * qs, sf);
+          word |= (m | (sign_bit(nr[e]) << 3)) << (4 * e);
+        }
+        if (live[p]) ((uint32_t*)(a.quant_out + (int64_t)t * (a.H / 2)))[slot[p]] = word;
+        // Scale bytes: lanes 8m..8m+7 hold blocks 4m'..4m'+3 (two lanes per block).
+        const uint32_t sf_here = live[p] ? sfc : 0u;
+        const uint32_t b1 = __shfl_down(sf_here, 2, 64);
+        const uint32_t b2 = __shfl_down(sf_here, 4, 64);
+        const uint32_t b3 = __shfl_down(sf_here, 6, 64);
+        const int s = slot[p];
+        if ((s & 7) == 0 && s < a.nv) {
+          const int b = s >> 1;                  // first block of the group of four
+          const int nb = a.H >> 4;
+          const uint32_t packed = sf_here | (b1 << 8) | (b2 << 16) | (b3 << 24);
+          if (a.sf_swizzled) {
+            const int nb4 = (nb + 3) & ~3;
+            const int64_t off = ((int64_t)(t >> 7) * (nb4 >> 2) + (b >> 2)) * 512 +
+                                (t & 31) * 16 + ((t & 127) >> 5) * 4;
+            *(uint32_t*)(a.sf_out + off) = packed;   // padding blocks carry sf 0
+          } else {
+            uint8_t* dst = a.sf_out + (int64_t)t * nb + b;
+            const uint8_t bytes[4] = {(uint8_t)sf_here, (uint8_t)b1, (uint8_t)b2, (uint8_t)b3};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (b + i < nb) dst[i] = bytes[i];
+          }
+        }
+      }
+    }
+  }
+
+  // Zero the swizzled scale rows between T and the next multiple of 128, spread over tokens.
+  if constexpr (MODE == MODE_NVFP4) {
+    if (a.sf_swizzled && slice == 0) {
+      const int nb4 = ((a.H >> 4) + 3) & ~3;
+      const int words = nb4 >> 2;
+      const int t_pad_end = (a.T + 127) & ~127;
+      for (int rr = a.T + t; rr < t_pad_end; rr += a.T) {
+        for (int i = tid; i < words; i += L) {
+          const int64_t off = ((int64_t)(rr >> 7) * words + i) * 512 + (rr & 31) * 16 +
+                              ((rr & 127) >> 5) * 4;
+          *(uint32_t*)(a.sf_out + off) = 0u;
+        }
+      }
+    }
+  }
+}
+
+// An empty kernel launched with a finalize entry point's grid, block and LDS: its duration is the
+// launch-latency floor that the small-batch timings are reported against.
+__global__ __launch_bounds__(1024) void launch_floor_kernel(int) {}
+
+// ------------------------------------------------------------------------------------------------
+// Host side: launch configuration and dispatch.
+// ------------------------------------------------------------------------------------------------
+struct Config {
+  int G, P, JMAX, L, span, grid_x;
+  size_t lds;
+};
+
+static int next_pow2(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+static void finish_config(int K, Config* c) {
+  int G = 1;
+  while (G < 4 && 2 * G * c->L <= 1024 && 2 * G <= K) G *= 2;
+  c->G = G;
+  const int J = (K + G - 1) / G;
+  c->JMAX = next_pow2(J < 4 ? 4 : J);
+  c->lds = (size_t)(G - 1) * c->P * c->L * 32;
+}
+
+// Slices per token for the split row modes: enough workgroups to put every CU to work
+// (about 1024 in total), each slice at least one wavefront of 8-element slots wide.
+// 1 = whole rows (no workspace needed).
+static int choose_slices(int64_t T, int nv) {
+  const int max_by_h = nv / 64;
+  int want = (int)((1024 + T - 1) / T);
+  int S = want < max_by_h ? want : max_by_h;
+  if (S > kMaxSlices) S = kMaxSlices;
+  for (; S > 1; --S) {
+    const int span = ((nv + S - 1) / S + 7) / 8 * 8;
+    const int s_eff = (nv + span - 1) / span;
+    if (s_eff == S) break;
+  }
+  return S < 1 ? 1 : S;
+}
+
+// Finalize-only: one workgroup per token and 64-slot slice. Row modes: one workgroup per token
+// and slice (slices = 1 covers the whole row with P slots per lane).
+static bool make_config(int mode, int H, int K, int slices, Config* c) {
+  const int nv = H / 8;
+  if (mode == MODE_FIN) {
+    c->P = 1;
+    c->L = 64;
+    c->span = 64;
+    c->grid_x = (nv + 63) / 64;
+  } else if (slices > 1) {
+    c->P = 1;
+    c->span = ((nv + slices - 1) / slices + 7) / 8 * 8;
+    c->L = (c->span + 63) / 64 * 64;
+    c->grid_x = slices;
+  } else {
+    c->P = nv <= 1024 ? 1 : (nv <= 2048 ? 2 : 0);
+    if (c->P == 0) return false;
+    c->L = ((nv + c->P - 1) / c->P + 63) / 64 * 64;
+    c->span = c->L * c->P;
+    c->grid_x = 1;
+  }
+  finish_config(K, c);
+  return true;
+}
+
+template <int ACT, int MODE, int G, int P, int JMAX>
+static hipError_t launch_one(const Params& p, const Config& c, hipStream_t s) {
+  dim3 grid((unsigned)(c.grid_x * p.T));
+  dim3 block(c.G * c.L);
+  hipLaunchKernelGGL((finalize_kernel<ACT, MODE, G, P, JMAX>), grid, block, c.lds, s, p);
+  return hipGetLastError();
+}
+
+template <int ACT, int MODE, int G, int P>
+static hipError_t dispatch_j(const Params& p, const Config& c, hipStream_t s) {
+  switch (c.JMAX) {
+    case 4: return launch_one<ACT, MODE, G, P, 4>(p, c, s);
+    case 8: return launch_one<ACT, MODE, G, P, 8>(p, c, s);
+    case 16: return launch_one<ACT, MODE, G, P, 16>(p, c, s);
+    case 32:
+      if constexpr (G <= 2) return launch_one<ACT, MODE, G, P, 32>(p, c, s);
+      break;
+    case 64:
+      if constexpr (G == 1) return launch_one<ACT, MODE, G, P, 64>(p, c, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int ACT, int MODE, int P>
+static hipError_t dispatch_g(const Params& p, const Config& c, hipStream_t s) {
+  switch (c.G) {
+    case 1: return dispatch_j<ACT, MODE, 1, P>(p, c, s);
+    case 2: return dispatch_j<ACT, MODE, 2, P>(p, c, s);
+    case 4: return dispatch_j<ACT, MODE, 4, P>(p, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int ACT, int MODE>
+static hipError_t dispatch_p(const Params& p, const Config& c, hipStream_t s) {
+  if (c.P == 1) return dispatch_g<ACT, MODE, 1>(p, c, s);
+  if constexpr (MODE != MODE_FIN) {
+    if (c.P == 2) return dispatch_g<ACT, MODE, 2>(p, c, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int MODE>
+static hipError_t dispatch(int act, const Params& p, const Config& c, hipStream_t s) {
+  return act == MOE_DTYPE_BF16 ? dispatch_p<ACT_BF16, MODE>(p, c, s)
+                               : dispatch_p<ACT_FP16, MODE>(p, c, s);
+}
+
+// ---- argument checks ----------------------------------------------------------------------------
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+};
+static bool overlap(Range x, Range y) { return x.lo < y.hi && y.lo < x.hi; }
+static Range rng(const void* p, size_t bytes) {
+  return Range{(uintptr_t)p, (uintptr_t)p + bytes};
+}
+
+struct Common {
+  const void* rows;
+  int64_t n_rows;
+  const int32_t* idx;
+  const void* scales;
+  int scales_dtype;
+  const void* shared;
+  float rsf;
+  int64_t T, H;
+  int K, act;
+};
+
+static int check_common(const Common& c, int h_multiple) {
+  if (c.act != MOE_DTYPE_BF16 && c.act != MOE_DTYPE_FP16) return MOE_FIN_ERR_DTYPE;
+  if (c.scales && c.scales_dtype != MOE_DTYPE_FP32 && c.scales_dtype != MOE_DTYPE_BF16)
+    return MOE_FIN_ERR_DTYPE;
+  if (c.K < 1 || c.K > 64) return MOE_FIN_ERR_BAD_TOPK;
+  if (c.H <= 0 || c.H % h_multiple != 0) return MOE_FIN_ERR_HIDDEN;
+  if (c.T < 0 || c.n_rows < 0) return MOE_FIN_ERR_BAD_SHAPE;
+  if (c.T > INT32_MAX / 2 || c.H > (int64_t)1 << 20 || c.n_rows > INT32_MAX)
+    return MOE_FIN_ERR_BAD_SHAPE;
+  return MOE_FIN_OK;
+}
+
+static int check_pointers(const Common& c) {
+  if (!c.idx || (c.n_rows > 0 && !c.rows)) return MOE_FIN_ERR_NULL_POINTER;
+  if (!aligned(c.rows, 16) || !aligned(c.idx, 4) || !aligned(c.shared, 16))
+    return MOE_FIN_ERR_ALIGNMENT;
+  if (c.scales && !aligned(c.scales, c.scales_dtype == MOE_DTYPE_FP32 ? 4 : 2))
+    return MOE_FIN_ERR_ALIGNMENT;
+  return MOE_FIN_OK;
+}
+
+static Params base_params(const Common& c) {
+  Params p;
+  memset(&p, 0, sizeof(p));
+  p.rows = (const uint8_t*)c.rows;
+  p.n_rows = c.n_rows;
+  p.idx = c.idx;
+  p.scales = c.scales;
+  p.scales_bf16 = c.scales_dtype == MOE_DTYPE_BF16;
+  p.shared = (const uint8_t*)c.shared;
+  p.rsf = c.rsf;
+  p.T = (int)c.T;
+  p.H = (int)c.H;
+  p.K = c.K;
+  p.nv = (int)(c.H / 8);
+  p.inv_h = 1.0f / (float)c.H;
+  return p;
+}
+
+static int to_code(hipError_t e) { return e == hipSuccess ? MOE_FIN_OK : MOE_FIN_ERR_HIP; }
+
+// All inputs of the finalize, for the overlap checks against the outputs.
+static int inputs_overlap(const Common& c, Range out) {
+  const size_t e = 2;
+  if (c.rows && overlap(out, rng(c.rows, (size_t)c.n_rows * c.H * e))) return 1;
+  if (overlap(out, rng(c.idx, (size_t)c.T * c.K * 4))) return 1;
+  if (c.scales && overlap(out, rng(c.scales, (size_t)c.T * c.K *
+                                                 (c.scales_dtype == MOE_DTYPE_FP32 ? 4 : 2))))
+    return 1;
+  if (c.shared && overlap(out, rng(c.shared, (size_t)c.T * c.H * e))) return 1;
+  return 0;
+}
+
+static size_t workspace_bytes_for(int64_t T) { return kWsHeader + (size_t)T * kWsPerToken; }
+
+static int run_rows(int mode, const Common& c, const void* residual, const void* gamma,
+                    float eps, void* residual_out, void* norm_out, const float* qscale,
+                    void* quant_out, void* scale_out, int sf_layout, void* workspace,
+                    void* stream) {
+  const int slices = workspace ? choose_slices(c.T, (int)(c.H / 8)) : 1;
+  Config cfg;
+  if (!make_config(mode, (int)c.H, c.K, slices, &cfg)) return MOE_FIN_ERR_HIDDEN;
+  if ((int64_t)cfg.grid_x * c.T > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
+  Params p = base_params(c);
+  p.residual = (const uint8_t*)residual;
+  p.gamma = (const uint8_t*)gamma;
+  p.eps = eps;
+  p.residual_out = (uint8_t*)residual_out;
+  p.out = (uint8_t*)norm_out;
+  p.quant_out = (uint8_t*)quant_out;
+  p.sf_out = (uint8_t*)scale_out;
+  p.qscale = qscale;
+  p.sf_swizzled = sf_layout == MOE_SF_SWIZZLED_128x4;
+  p.lanes = cfg.L;
+  p.slot_span = cfg.span;
+  p.slices = cfg.grid_x;
+  p.ws = (uint8_t*)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  switch (mode) {
+    case MODE_RMS: return to_code(dispatch<MODE_RMS>(c.act, p, cfg, s));
+    case MODE_NVFP4: return to_code(dispatch<MODE_NVFP4>(c.act, p, cfg, s));
+    case MODE_FP8: return to_code(dispatch<MODE_FP8>(c.act, p, cfg, s));
+  }
+  return MOE_FIN_ERR_QUANT_TYPE;
+}
+
+// Validation shared by the residual + RMSNorm entry points.
+static int check_rows(const Common& c, const void* residual, const void* gamma,
+                      const void* residual_out, const void* norm_out, bool norm_required) {
+  if (!residual || !gamma || (norm_required && !norm_out)) return MOE_FIN_ERR_NULL_POINTER;
+  if (!aligned(residual, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) ||
+      !aligned(norm_out, 16))
+    return MOE_FIN_ERR_ALIGNMENT;
+  const size_t tb = (size_t)c.T * c.H * 2;
+  if (norm_out) {
+    Range o = rng(norm_out, tb);
+    if (inputs_overlap(c, o) || overlap(o, rng(residual, tb)) ||
+        overlap(o, rng(gamma, (size_t)c.H * 2)))
+      return MOE_FIN_ERR_ALIAS;
+    if (residual_out && overlap(o, rng(residual_out, tb))) return MOE_FIN_ERR_ALIAS;
+  }
+  if (residual_out) {
+    Range o = rng(residual_out, tb);
+    if (inputs_overlap(c, o) || overlap(o, rng(gamma, (size_t)c.H * 2)))
+      return MOE_FIN_ERR_ALIAS;
+    if (residual_out != residual && overlap(o, rng(residual, tb))) return MOE_FIN_ERR_ALIAS;
+  }
+  return MOE_FIN_OK;
+}
+
+// Workspace of the split row modes: NULL (whole rows) or at least workspace_bytes_for(T) bytes,
+// 256-byte aligned, overlapping no other buffer.
+static int check_workspace(const Common& c, const void* ws, size_t ws_bytes,
+                           std::initializer_list<Range> others) {
+  if (!ws) return MOE_FIN_OK;
+  if (!aligned(ws, 256)) return MOE_FIN_ERR_ALIGNMENT;
+  if (ws_bytes < workspace_bytes_for(c.T)) return MOE_FIN_ERR_WORKSPACE;
+  Range w = rng(ws, ws_bytes);
+  if (inputs_overlap(c, w)) return MOE_FIN_ERR_ALIAS;
+  for (const Range& o : others)
+    if (o.hi > o.lo && overlap(w, o)) return MOE_FIN_ERR_ALIAS;
+  return MOE_FIN_OK;
+}
+
+}  // namespace mfin
+
+using namespace mfin;
+
+extern "C" {
+
+int moe_finalize_version(void) { return 100; }
+
+const char* moe_finalize_error_string(int code) {
+  switch (code) {
+    case MOE_FIN_OK: return "success";
+    case MOE_FIN_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case MOE_FIN_ERR_BAD_SHAPE: return "negative or oversized num_tokens / num_permuted_rows";
+    case MOE_FIN_ERR_BAD_TOPK: return "top_k outside [1, 64]";
+    case MOE_FIN_ERR_HIDDEN:
+      return "hidden must be positive and a multiple of 8 (16 for NVFP4), at most 16384 for the "
+             "RMSNorm entry points";
+    case MOE_FIN_ERR_ALIGNMENT: return "a pointer is not aligned as required";
+    case MOE_FIN_ERR_DTYPE: return "unknown act_dtype or scales_dtype";
+    case MOE_FIN_ERR_QUANT_TYPE: return "unknown quant_type";
+    case MOE_FIN_ERR_SF_LAYOUT: return "scale layout must be LINEAR or SWIZZLED_128x4";
+    case MOE_FIN_ERR_ALIAS: return "an output overlaps an input or another output";
+    case MOE_FIN_ERR_HIP: return "the HIP runtime refused the kernel launch";
+    case MOE_FIN_ERR_WORKSPACE:
+      return "workspace smaller than moe_finalize_workspace_size(num_tokens, hidden, top_k)";
+  }
+  return "unknown error code";
+}
+
+size_t moe_finalize_sf_size(int64_t num_tokens, int64_t hidden, int sf_layout) {
+  if (num_tokens < 0 || hidden < 0) return 0;
+  const int64_t nb = hidden / 16;
+  if (sf_layout == MOE_SF_SWIZZLED_128x4)
+    return (size_t)((num_tokens + 127) / 128 * 128) * (size_t)((nb + 3) / 4 * 4);
+  if (sf_layout == MOE_SF_LINEAR) return (size_t)(num_tokens * nb);
+  return 0;
+}
+
+size_t moe_finalize_workspace_size(int64_t num_tokens, int64_t hidden, int top_k) {
+  (void)hidden;
+  (void)top_k;
+  if (num_tokens < 0) return 0;
+  return workspace_bytes_for(num_tokens);
+}
+
+int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden, int top_k,
+                                  void* stream) {
+  if (entry < 0 || entry > 2) return MOE_FIN_ERR_QUANT_TYPE;
+  if (top_k < 1 || top_k > 64) return MOE_FIN_ERR_BAD_TOPK;
+  if (hidden <= 0 || hidden % 8 != 0 || (entry > 0 && hidden > 16384)) return MOE_FIN_ERR_HIDDEN;
+  if (num_tokens < 0 || num_tokens > INT32_MAX / 2) return MOE_FIN_ERR_BAD_SHAPE;
+  if (num_tokens == 0) return MOE_FIN_OK;
+  Config c;
+  make_config(entry == 0 ? MODE_FIN : MODE_RMS, (int)hidden, top_k,
+              entry == 0 ? 1 : choose_slices(num_tokens, (int)(hidden / 8)), &c);
+  if ((int64_t)c.grid_x * num_tokens > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
+  hipLaunchKernelGGL(launch_floor_kernel, dim3((unsigned)(c.grid_x * num_tokens)), dim3(c.G * c.L),
+                     c.lds, (hipStream_t)stream, 0);
+  return to_code(hipGetLastError());
+}
+
+int moe_finalize_run(const void* permuted_rows, int64_t num_permuted_rows,
+                     const int32_t* expanded_idx_to_permuted_idx, const void* expert_scales,
+                     int scales_dtype, const void* shared_expert_output,
+                     float routed_scaling_factor, void* out, int64_t num_tokens, int64_t hidden,
+                     int top_k, int act_dtype, void* stream) {
+  Common c{permuted_rows, num_permuted_rows, expanded_idx_to_permuted_idx, expert_scales,
+           scales_dtype, shared_expert_output, routed_scaling_factor, num_tokens, hidden,
+           top_k, act_dtype};
+  int rc = check_common(c, 8);
+  if (rc) return rc;
+  if (num_tokens == 0) return MOE_FIN_OK;
+  if ((rc = check_pointers(c))) return rc;
+  if (!out) return MOE_FIN_ERR_NULL_POINTER;
+  if (!aligned(out, 16)) return MOE_FIN_ERR_ALIGNMENT;
+  if (inputs_overlap(c, rng(out, (size_t)num_tokens * hidden * 2))) return MOE_FIN_ERR_ALIAS;
+  Config cfg;
+  make_config(MODE_FIN, (int)hidden, top_k, 1, &cfg);
+  if ((int64_t)cfg.grid_x * num_tokens > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
+  Params p = base_params(c);
+  p.out = (uint8_t*)out;
+  p.lanes = cfg.L;
+  p.slot_span = cfg.span;
+  p.slices = cfg.grid_x;
+  return to_code(dispatch<MODE_FIN>(act_dtype, p, cfg, (hipStream_t)stream));
+}
+
+int moe_finalize_rmsnorm_run(const void* permuted_rows, int64_t num_permuted_rows,
+                             const int32_t* expanded_idx_to_permuted_idx,
+                             const void* expert_scales, int scales_dtype,
+                             const void* shared_expert_output, float routed_scaling_factor,
+                             const void* residual, const void* gamma, float eps,
+                             void* residual_out, void* norm_out, void* workspace,
+                             size_t workspace_bytes, int64_t num_tokens, int64_t hidden,
+                             int top_k, int act_dtype, void* stream) {
+  Common c{permuted_rows, num_permuted_rows, expanded_idx_to_permuted_idx, expert_scales,
+           scales_dtype, shared_expert_output, routed_scaling_factor, num_tokens, hidden,
+           top_k, act_dtype};
+  int rc = check_common(c, 8);
+  if (rc) return rc;
+  if (hidden > 16384) return MOE_FIN_ERR_HIDDEN;
+  if (num_tokens == 0) return MOE_FIN_OK;
+  if ((rc = check_pointers(c))) return rc;
+  if ((rc = check_rows(c, residual, gamma, residual_out, norm_out, true))) return rc;
+  const size_t tb = (size_t)num_tokens * hidden * 2;
+  if ((rc = check_workspace(c, workspace, workspace_bytes,
+                            {rng(residual, tb), rng(gamma, (size_t)hidden * 2),
+                             residual_out ? rng(residual_out, tb) : Range{0, 0},
+                             rng(norm_out, tb)})))
+    return rc;
+  return run_rows(MODE_RMS, c, residual, gamma, eps, residual_out, norm_out, nullptr, nullptr,
+                  nullptr, 0, workspace, stream);
+}
+
+int moe_finalize_quant_run(const void* permuted_rows, int64_t num_permuted_rows,
+                           const int32_t* expanded_idx_to_permuted_idx, const void* expert_scales,
+                           int scales_dtype, const void* shared_expert_output,
+                           float routed_scaling_factor, const void* residual, const void* gamma,
+                           float eps, int quant_type, const float* quant_scale, void* quant_out,
+                           void* scale_out, int sf_layout, void* residual_out, void* norm_out,
+                           void* workspace, size_t workspace_bytes, int64_t num_tokens,
+                           int64_t hidden, int top_k, int act_dtype, void* stream) {
+  Common c{permuted_rows, num_permuted_rows, expanded_idx_to_permuted_idx, expert_scales,
+           scales_dtype, shared_expert_output, routed_scaling_factor, num_tokens, hidden,
+           top_k, act_dtype};
+  if (quant_type != MOE_QUANT_NVFP4 && quant_type != MOE_QUANT_FP8_E4M3)
+    return MOE_FIN_ERR_QUANT_TYPE;
+  const bool nvfp4 = quant_type == MOE_QUANT_NVFP4;
+  if (nvfp4 && sf_layout != MOE_SF_LINEAR && sf_layout != MOE_SF_SWIZZLED_128x4)
+    return MOE_FIN_ERR_SF_LAYOUT;
+  int rc = check_common(c, nvfp4 ? 16 : 8);
+  if (rc) return rc;
+  if (hidden > 16384) return MOE_FIN_ERR_HIDDEN;
+  if (num_tokens == 0) return MOE_FIN_OK;
+  if ((rc = check_pointers(c))) return rc;
+  if ((rc = check_rows(c, residual, gamma, residual_out, norm_out, false))) return rc;
+  if (!quant_scale || !quant_out || (nvfp4 && !scale_out)) return MOE_FIN_ERR_NULL_POINTER;
+  if (!aligned(quant_scale, 4) || !aligned(quant_out, 16) || (nvfp4 && !aligned(scale_out, 4)))
+    return MOE_FIN_ERR_ALIGNMENT;
+  const size_t qbytes = (size_t)num_tokens * hidden / (nvfp4 ? 2 : 1);
+  const size_t sbytes = nvfp4 ? moe_finalize_sf_size(num_tokens, hidden, sf_layout) : 0;
+  const size_t tb = (size_t)num_tokens * hidden * 2;
+  Range q = rng(quant_out, qbytes);
+  if (inputs_overlap(c, q) || overlap(q, rng(residual, tb)) ||
+      overlap(q, rng(gamma, (size_t)hidden * 2)) ||
+      (residual_out && overlap(q, rng(residual_out, tb))) ||
+      (norm_out && overlap(q, rng(norm_out, tb))) || overlap(q, rng(quant_scale, 4)))
+    return MOE_FIN_ERR_ALIAS;
+  if (nvfp4) {
+    Range sr = rng(scale_out, sbytes);
+    if (inputs_overlap(c, sr) || overlap(sr, q) || overlap(sr, rng(residual, tb)) ||
+        overlap(sr, rng(gamma, (size_t)hidden * 2)) ||
+        (residual_out && overlap(sr, rng(residual_out, tb))) ||
+        (norm_out && overlap(sr, rng(norm_out, tb))) || overlap(sr, rng(quant_scale, 4)))
+      return MOE_FIN_ERR_ALIAS;
+  }
+  if ((rc = check_workspace(c, workspace, workspace_bytes,
+                            {rng(residual, tb), rng(gamma, (size_t)hidden * 2),
+                             residual_out ? rng(residual_out, tb) : Range{0, 0},
+                             norm_out ? rng(norm_out, tb) : Range{0, 0}, q,
+                             nvfp4 ? rng(scale_out, sbytes) : Range{0, 0},
+                             rng(quant_scale, 4)})))
+    return rc;
+  return run_rows(nvfp4 ? MODE_NVFP4 : MODE_FP8, c, residual, gamma, eps, residual_out, norm_out,
+                  quant_scale, quant_out, scale_out, sf_layout, workspace, stream);
+}
+
+}  // extern "C"

@@ -51,6 +51,13 @@ def bits_to_values(bits, act_dtype):
     return O.decode_bits(bits, O.FORMATS[act_dtype])
 
 
+def spacing(x, act_dtype) -> np.ndarray:
+    """Distance from |x| to the next larger value of the format (its ulp)."""
+    fmt = O.FORMATS[act_dtype]
+    _, E = np.frexp(np.abs(np.asarray(x, dtype=np.float64)))
+    return np.ldexp(1.0, np.maximum(E - 1, fmt.emin) - fmt.frac_bits)
+
+
 def outside(values, lo, hi) -> np.ndarray:
     """Mask of elements outside [lo, hi] (NaN counts as outside)."""
     v = np.asarray(values, dtype=np.float64)

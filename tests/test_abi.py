@@ -1,0 +1,139 @@
+"""The C ABI on the CPU: the library loads, exports every symbol include/moe_finalize.h declares,
+and rejects bad arguments with the documented codes before touching the GPU (no launches here;
+every call below fails its host-side checks or is the T = 0 no-op)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import moe_expert_output_amd as M
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_finalize.h")
+LIB = M.LIB
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared()
+    assert set(names) == set(M.EXPORTED), names
+    for n in names:
+        assert hasattr(LIB, n), n
+
+
+def _header_consts():
+    return {k: int(v) for k, v in re.findall(r"#define (MOE_\w+) \(?(-?\d+)\)?", open(HEADER).read())}
+
+
+def test_binding_constants_match_header():
+    c = _header_consts()
+    assert c["MOE_DTYPE_BF16"] == M.MOE_DTYPE_BF16 and c["MOE_DTYPE_FP16"] == M.MOE_DTYPE_FP16
+    assert c["MOE_QUANT_NVFP4"] == M.MOE_QUANT_NVFP4
+    assert c["MOE_QUANT_FP8_E4M3"] == M.MOE_QUANT_FP8_E4M3
+    assert c["MOE_SF_SWIZZLED_128x4"] == M.MOE_SF_SWIZZLED_128x4
+    assert c["MOE_SF_LINEAR"] == M.MOE_SF_LINEAR
+
+
+def test_error_strings():
+    for name, code in _header_consts().items():
+        if name.startswith("MOE_FIN_ERR"):
+            s = M.moe_finalize_error_string(code)
+            assert s and s != "unknown error code", name
+    assert M.moe_finalize_error_string(12345) == "unknown error code"
+
+
+@pytest.mark.parametrize("T,H", [(1, 64), (5, 48), (64, 6144), (128, 7168), (130, 96), (0, 64)])
+def test_sf_size_matches_oracle(T, H):
+    for layout in (M.MOE_SF_LINEAR, M.MOE_SF_SWIZZLED_128x4):
+        assert M.moe_finalize_sf_size(T, H, layout) == O.sf_size(T, H, layout)
+    assert M.moe_finalize_sf_size(T, H, 7) == 0
+
+
+# fake, never-dereferenced device addresses
+A = 0x7F0000000000
+B = 0x7F0010000000
+C = 0x7F0020000000
+D = 0x7F0030000000
+E = 0x7F0040000000
+
+
+def fin(rows=A, n_rows=64, idx=B, scales=C, sdt=2, shared=None, rsf=2.5, out=D, T=4, H=1024,
+        K=8, act=0):
+    return LIB.moe_finalize_run(rows, n_rows, idx, scales, sdt, shared, rsf, out, T, H, K, act,
+                                None)
+
+
+WS = 0x7F0050000000
+
+
+def rms(rows=A, n_rows=64, idx=B, scales=C, sdt=2, shared=None, residual=E, gamma=E + 0x100000,
+        eps=1e-6, res_out=E + 0x200000, norm_out=D, ws=None, ws_bytes=0, T=4, H=1024, K=8, act=0):
+    return LIB.moe_finalize_rmsnorm_run(rows, n_rows, idx, scales, sdt, shared, 2.5, residual,
+                                        gamma, eps, res_out, norm_out, ws, ws_bytes, T, H, K, act,
+                                        None)
+
+
+def quant(qt=1, qs=E + 0x300000, qo=E + 0x400000, so=E + 0x500000, layout=1, H=1024, T=4,
+          norm_out=D, ws=None, ws_bytes=0):
+    return LIB.moe_finalize_quant_run(A, 64, B, C, 2, None, 2.5, E, E + 0x100000, 1e-6, qt, qs,
+                                      qo, so, layout, E + 0x200000, norm_out, ws, ws_bytes, T, H,
+                                      8, 0, None)
+
+
+def test_validation_codes():
+    assert fin(K=0) == -3 and fin(K=65) == -3
+    assert fin(act=5) == -6 and fin(sdt=9) == -6
+    assert fin(H=1020) == -4 and fin(H=0) == -4
+    assert fin(T=-1) == -2 and fin(n_rows=-1) == -2
+    assert fin(T=0) == 0                       # no-op, nothing touched
+    assert fin(T=0, idx=None, out=None) == 0
+    assert fin(idx=None) == -1 and fin(out=None) == -1
+    assert fin(rows=None) == -1
+    assert fin(rows=A + 8) == -5 and fin(out=D + 2) == -5 and fin(idx=B + 2) == -5
+    assert fin(scales=C + 2) == -5             # fp32 scales need 4-byte alignment
+    assert fin(out=A + 4096) == -9             # output inside the permuted rows
+    assert fin(out=B) == -9
+
+
+def test_rmsnorm_validation_codes():
+    assert rms(H=16392) == -4
+    assert rms(residual=None) == -1 and rms(gamma=None) == -1 and rms(norm_out=None) == -1
+    assert rms(res_out=E + 8) == -5
+    assert rms(norm_out=E) == -9               # norm_out overlaps residual
+    assert rms(res_out=D) == -9                # residual_out overlaps norm_out
+    assert rms(T=0) == 0
+    need = M.moe_finalize_workspace_size(4, 1024, 8)
+    assert need == 256 + 4 * 512
+    assert rms(ws=WS + 64, ws_bytes=need) == -5           # workspace must be 256-byte aligned
+    assert rms(ws=WS, ws_bytes=need - 1) == -11           # too small
+    assert rms(ws=E, ws_bytes=need) == -9                 # overlaps residual
+    assert rms(ws=A + 256, ws_bytes=need) == -9           # overlaps the permuted rows
+    assert quant(ws=WS, ws_bytes=16) == -11
+    assert quant(ws=E + 0x400000, ws_bytes=need) == -9    # overlaps quant_out
+
+
+def test_launch_floor_validation_codes():
+    f = LIB.moe_finalize_launch_floor_run
+    assert f(3, 4, 1024, 8, None) == -7 and f(-1, 4, 1024, 8, None) == -7
+    assert f(1, 4, 1024, 0, None) == -3 and f(1, 4, 1020, 8, None) == -4
+    assert f(1, 4, 16392, 8, None) == -4 and f(1, -1, 1024, 8, None) == -2
+    assert f(1, 0, 1024, 8, None) == 0
+
+
+def test_quant_validation_codes():
+    assert quant(qt=0) == -7 and quant(qt=3) == -7
+    assert quant(layout=2) == -8               # SWIZZLED_8x4 is not accepted
+    assert quant(H=1032) == -4                 # NVFP4 needs hidden % 16 == 0
+    assert quant(qs=None) == -1 and quant(qo=None) == -1 and quant(so=None) == -1
+    assert quant(qo=E + 0x400008) == -5
+    assert quant(so=A) == -9
+    assert quant(T=0) == 0

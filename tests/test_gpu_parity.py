@@ -1,0 +1,413 @@
+"""GPU parity: the HIP path through the C ABI against the FP64 oracle on seeded inputs.
+
+Comparison rules (see tests/comparators.py): finalize values inside the float32 admissible
+window of the exact sum (and within 1 ulp except near cancellation); residual_out inside the
+image of that window; norm_out within 1 ulp of the oracle where residual_out matched it;
+indices / route selection bit-exact (dyadic fixtures, exact gathers, NaN poison); quantized codes
+bit-exact where the kernel's norm_out equals the oracle's.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU containers
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import moe_expert_output_amd as M  # noqa: E402
+import oracle as O  # noqa: E402
+from synth import make_inputs, workload_seed  # noqa: E402
+from tests.parity import (bits16, check_finalize, check_norm, check_residual,  # noqa: E402
+                          np64, oracle_ref, to_dev)
+
+ACT_T = {"bf16": torch.bfloat16, "fp16": torch.float16}
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def run_finalize(inp, d=None, rsf=None):
+    d = d or to_dev(inp)
+    out = torch.empty(inp.T, inp.H, dtype=ACT_T[inp.act_dtype], device="cuda")
+    M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"],
+                       inp.rsf if rsf is None else rsf, out)
+    torch.cuda.synchronize()
+    return out
+
+
+_WS = {}
+
+
+def workspace(T, H=0, K=0):
+    """A zero-filled workspace shared by the tests (calls are serialized on one stream)."""
+    need = M.moe_finalize_workspace_size(T, H, K)
+    ws = _WS.get("ws")
+    if ws is None or ws.numel() < need:
+        ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device="cuda")
+        _WS["ws"] = ws
+    return ws
+
+
+def ws_flag():
+    ws = _WS.get("ws")
+    return 0 if ws is None else int(ws[:4].view(torch.int32).item())
+
+
+def run_rmsnorm(inp, d=None, residual_out=True, use_ws=True):
+    d = d or to_dev(inp)
+    dt = ACT_T[inp.act_dtype]
+    ro = torch.empty(inp.T, inp.H, dtype=dt, device="cuda") if residual_out else None
+    no = torch.empty(inp.T, inp.H, dtype=dt, device="cuda")
+    ws = workspace(inp.T) if use_ws else None
+    M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                               d["residual"], d["gamma"], inp.eps, ro, no, ws)
+    torch.cuda.synchronize()
+    assert ws_flag() == 0, "a split row timed out waiting for its slices"
+    return ro, no
+
+
+def full_check(inp, *, finalize=True, rmsnorm=True):
+    _say(f"case T={inp.T} H={inp.H} K={inp.K} act={inp.act_dtype} scales={inp.scale_dtype} "
+         f"seed={inp.seed} shared={inp.shared is not None}")
+    ref = oracle_ref(inp, with_norm=rmsnorm)
+    reps = []
+    d = to_dev(inp)
+    if finalize:
+        s = run_finalize(inp, d)
+        reps.append(check_finalize(np64(s), ref, inp.act_dtype))
+    if rmsnorm:
+        for use_ws in (True, False):      # split rows (workspace) and whole-row workgroups
+            ro, no = run_rmsnorm(inp, d, use_ws=use_ws)
+            R, N = np64(ro), np64(no)
+            reps.append(check_residual(R, ref, np64(inp.residual), inp.act_dtype))
+            reps.append(check_norm(N, R, ref, np64(inp.gamma), inp.eps, inp.act_dtype))
+        # mean absolute error vs the unrounded FP64 reference, as the pages report it
+        ref_res, ref_norm = O.reference_unrounded(np64(inp.rows), inp.idx.numpy(),
+                                                  np64(inp.scales), np64(inp.shared), inp.rsf,
+                                                  np64(inp.residual), np64(inp.gamma), inp.eps)
+        _say(f"  mean|err| residual_out {np.abs(R - ref_res).mean():.3e} "
+             f"(floor {np.abs(ref.R - ref_res).mean():.3e}), norm_out "
+             f"{np.abs(N - ref_norm).mean():.3e}")
+    for r in reps:
+        _say("  ", r)
+    return reps
+
+
+# ---- the workloads -------------------------------------------------------------------------------
+def test_tiny_t4_h1024_k8():
+    full_check(make_inputs(4, 1024, 8, seed=workload_seed("tiny", 4)))
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_decode_h6144_k8(T):
+    full_check(make_inputs(T, 6144, 8, seed=workload_seed("decode", T)))
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+@pytest.mark.parametrize("T", [32, 64, 128])
+def test_larger_decode_h7168_k8(T, act):
+    full_check(make_inputs(T, 7168, 8, act_dtype=act, seed=workload_seed("larger", T, act)))
+
+
+@pytest.mark.parametrize("HK", [(2048, 22), (3584, 16), (2048, 6), (2048, 10)])
+@pytest.mark.parametrize("sdt", ["fp32", "bf16"])
+@pytest.mark.parametrize("T", [1, 8, 16, 32])
+def test_high_topk(T, sdt, HK):
+    H, K = HK
+    full_check(make_inputs(T, H, K, scale_dtype=sdt, with_shared=False,
+                           seed=workload_seed("highk", T, "bf16", sdt, K)))
+
+
+# ---- exactness: indices, route selection, poison -------------------------------------------------
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+def test_k1_exact_gather(act):
+    inp = make_inputs(37, 1032, 1, seed=71, act_dtype=act, scale_dtype=None, with_shared=False,
+                      n_rows=80)
+    s = run_finalize(inp, rsf=1.0)
+    want = torch.zeros(37, 1032, dtype=ACT_T[act])
+    for t in range(37):
+        p = int(inp.idx[t, 0])
+        if p >= 0:
+            want[t] = inp.rows[p]
+    assert np.array_equal(bits16(s), bits16(want))
+
+
+def _dyadic_inputs(T, H, K, act, seed):
+    """Small-integer rows, power-of-two weights, RSF 2, integer shared and residual: every float32
+    operation is exact, so finalize and residual_out must match the oracle bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n_rows = T * K + 5
+    inp = make_inputs(T, H, K, seed=seed, act_dtype=act, n_rows=n_rows)
+    dt = ACT_T[act]
+    inp.rows = torch.from_numpy(rng.integers(-8, 9, (n_rows, H)).astype(np.float32)).to(dt)
+    inp.scales = torch.from_numpy(
+        np.ldexp(1.0, rng.integers(-4, 2, (T, K))).astype(np.float32))
+    inp.shared = torch.from_numpy(rng.integers(-16, 17, (T, H)).astype(np.float32)).to(dt)
+    inp.residual = torch.from_numpy(rng.integers(-16, 17, (T, H)).astype(np.float32)).to(dt)
+    inp.rsf = 2.0
+    return inp
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+@pytest.mark.parametrize("TK", [(3, 8), (16, 22), (5, 64), (9, 6)])
+def test_dyadic_bit_exact(act, TK):
+    T, K = TK
+    H = 2048 if act == "bf16" else 1024
+    inp = _dyadic_inputs(T, H, K, act, seed=80 + K)
+    ref = oracle_ref(inp)
+    s = run_finalize(inp)
+    assert np.array_equal(bits16(s), O.encode_bits(ref.s, O.FORMATS[act]).astype(np.int64))
+    ro, no = run_rmsnorm(inp)
+    assert np.array_equal(np64(ro), ref.R)
+    check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, act)
+    # routes reordered inside the top-k: bit-identical (every operation is exact)
+    prng = np.random.Generator(np.random.PCG64(7 + K))
+    perm = torch.from_numpy(np.stack([prng.permutation(K) for _ in range(T)]))
+    inp2 = _dyadic_inputs(T, H, K, act, seed=80 + K)
+    inp2.idx = torch.gather(inp.idx, 1, perm)
+    inp2.scales = torch.gather(inp.scales, 1, perm)
+    assert np.array_equal(bits16(run_finalize(inp2)), bits16(s))
+
+
+def test_nan_poison_never_read():
+    inp = make_inputs(24, 2048, 10, seed=90, n_rows=400)
+    ref = oracle_ref(inp)
+    used = set(int(p) for p in inp.idx.flatten().tolist() if p >= 0)
+    rows = inp.rows.clone()
+    for r in range(inp.n_rows):
+        if r not in used:
+            rows[r] = float("nan")
+    sc = inp.scales.clone()
+    sc[inp.idx < 0] = float("nan")
+    inp.rows, inp.scales = rows, sc
+    s = run_finalize(inp)
+    ro, no = run_rmsnorm(inp)
+    for t in (s, ro, no):
+        assert torch.isfinite(t.float()).all()
+    check_finalize(np64(s), ref, "bf16")
+    # out-of-range indices on both sides are absent routes too
+    inp.idx = torch.where(inp.idx < 0, torch.full_like(inp.idx, 1 << 30), inp.idx)
+    assert np.array_equal(bits16(run_finalize(inp)), bits16(s))
+    inp.idx = torch.where(inp.idx == (1 << 30), torch.full_like(inp.idx, -7), inp.idx)
+    assert np.array_equal(bits16(run_finalize(inp)), bits16(s))
+
+
+def test_no_valid_routes_and_no_rows():
+    inp = make_inputs(6, 1024, 8, seed=91)
+    inp.idx[2] = -1
+    inp.idx[4] = -1
+    full_check(inp)
+    s = run_finalize(inp)
+    assert np.array_equal(bits16(s[2]), bits16(inp.shared[2]))
+    # zero permuted rows: every route absent
+    inp0 = make_inputs(3, 512, 4, seed=92, with_shared=False)
+    inp0.rows = inp0.rows[:0]
+    inp0.n_rows = 0
+    s0 = run_finalize(inp0)
+    assert not s0.float().abs().sum().item()
+
+
+# ---- edge shapes ------------------------------------------------------------------------------------
+@pytest.mark.parametrize("H", [8, 1000, 1032, 4104, 8192, 12288, 16384])
+def test_ragged_and_large_hidden(H):
+    full_check(make_inputs(5, H, 8, seed=100 + H))
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 5, 17, 33, 64])
+def test_topk_range(K):
+    full_check(make_inputs(7, 2048, K, seed=200 + K, mask_frac=0.25 if K > 1 else 0.0))
+
+
+def test_zero_tokens_is_noop():
+    inp = make_inputs(1, 1024, 8, seed=300)
+    d = to_dev(inp)
+    out = torch.full((1, 1024), 7.0, dtype=torch.bfloat16, device="cuda")
+    M.moe_finalize_run(d["rows"], d["idx"][:0], d["scales"][:0], None, 2.5, out[:0])
+    M.moe_finalize_rmsnorm_run(d["rows"], d["idx"][:0], d["scales"][:0], None, 2.5,
+                               d["residual"][:0], d["gamma"], 1e-6, None, out[:0])
+    torch.cuda.synchronize()
+    assert (out.float() == 7.0).all()
+
+
+def test_optional_terms_and_inplace_residual():
+    inp = make_inputs(9, 3072, 8, seed=301)
+    ref = oracle_ref(inp)
+    d = to_dev(inp)
+    # in-place: residual_out aliases residual
+    res = d["residual"].clone()
+    no = torch.empty_like(res)
+    M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf, res,
+                               d["gamma"], inp.eps, res, no, workspace(inp.T))
+    torch.cuda.synchronize()
+    check_residual(np64(res), ref, np64(inp.residual), "bf16")
+    # residual_out omitted: norm_out unchanged
+    _, no2 = run_rmsnorm(inp, d, residual_out=False)
+    assert np.array_equal(bits16(no2), bits16(no))
+    # scales omitted == all-ones scales; shared omitted; RSF 1
+    inp1 = make_inputs(9, 3072, 8, seed=302, with_shared=False)
+    inp1.scales = None
+    full_check(inp1)
+
+
+def test_deterministic_and_graph_replay():
+    inp = make_inputs(64, 7168, 8, seed=303)
+    d = to_dev(inp)
+    ro1, no1 = run_rmsnorm(inp, d)
+    ro2, no2 = run_rmsnorm(inp, d)
+    assert np.array_equal(bits16(ro1), bits16(ro2)) and np.array_equal(bits16(no1), bits16(no2))
+    ro = torch.empty_like(ro1)
+    no = torch.empty_like(no1)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    ws = workspace(inp.T)
+    with torch.cuda.graph(g, stream=s):
+        M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                   d["residual"], d["gamma"], inp.eps, ro, no, ws)
+    for _ in range(3):
+        ro.zero_()
+        no.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits16(ro), bits16(ro1)) and np.array_equal(bits16(no), bits16(no1))
+    assert ws_flag() == 0
+
+
+def test_workspace_shared_across_shapes():
+    """One workspace, calls whose rows split into different slice counts, in any order."""
+    cases = [(1, 6144), (128, 7168), (16, 6144), (4, 1024), (64, 7168), (1, 7168), (32, 3584)]
+    for T, H in cases + cases[::-1]:
+        inp = make_inputs(T, H, 8, seed=400 + T + H)
+        ref = oracle_ref(inp)
+        ro, no = run_rmsnorm(inp)
+        check_residual(np64(ro), ref, np64(inp.residual), "bf16")
+        check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, "bf16")
+    assert ws_flag() == 0
+
+
+# ---- validation through the ABI on a device ---------------------------------------------------------
+def test_validation_errors():
+    inp = make_inputs(4, 1024, 8, seed=304)
+    d = to_dev(inp)
+    out = torch.empty(4, 1024, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(M.MoeFinalizeError) as e:
+        M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"], 2.5, d["rows"][:4])
+    assert e.value.code == -9  # output overlaps an input
+    buf = torch.empty(4 * 1024 + 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(M.MoeFinalizeError) as e:
+        M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"], 2.5,
+                           buf[1:1 + 4096].view(4, 1024))
+    assert e.value.code == -5  # misaligned output
+    out.fill_(3.0)
+    torch.cuda.synchronize()
+    assert (out.float() == 3.0).all()
+
+
+# ---- quantized outputs -------------------------------------------------------------------------------
+def _sf_offsets(T, H, layout):
+    return np.array([[O.sf_offset(t, b, H, layout) for b in range(H // 16)] for t in range(T)])
+
+
+def run_quant(inp, qtype, qscale, layout=M.MOE_SF_SWIZZLED_128x4, with_norm=True, use_ws=True):
+    d = to_dev(inp)
+    dt = ACT_T[inp.act_dtype]
+    T, H = inp.T, inp.H
+    ro = torch.empty(T, H, dtype=dt, device="cuda")
+    no = torch.empty(T, H, dtype=dt, device="cuda") if with_norm else None
+    nv = qtype == M.MOE_QUANT_NVFP4
+    qo = torch.full((T, H // 2 if nv else H), 0xAB, dtype=torch.uint8, device="cuda")
+    so = None
+    if nv:
+        so = torch.full((M.moe_finalize_sf_size(T, H, layout),), 0xCD, dtype=torch.uint8,
+                        device="cuda")
+    qs = torch.tensor([qscale], dtype=torch.float32, device="cuda")
+    M.moe_finalize_quant_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                             d["residual"], d["gamma"], inp.eps, qtype, qs, qo, so, layout, ro,
+                             no, workspace(T) if use_ws else None)
+    torch.cuda.synchronize()
+    assert ws_flag() == 0
+    return ro, no, qo.cpu().numpy(), (None if so is None else so.cpu().numpy())
+
+
+@pytest.mark.parametrize("layout", [1, 0])
+@pytest.mark.parametrize("TH", [(64, 6144), (5, 1024), (130, 2048), (1, 48)])
+def test_nvfp4(TH, layout):
+    T, H = TH
+    inp = make_inputs(T, H, 8, seed=workload_seed("quant", T) + H)
+    _say(f"nvfp4 T={T} H={H} layout={layout}")
+    ref = oracle_ref(inp)
+    gs = O.nvfp4_global_scale(ref.N)            # 448 * 6 / amax(norm_out), as float32
+    codes_or, sf_or = O.quant_nvfp4(ref.N, gs, layout)
+    offs = _sf_offsets(T, H, layout)
+    for use_ws in (True, False):
+        ro, no, qo, so = run_quant(inp, M.MOE_QUANT_NVFP4, gs, layout, use_ws=use_ws)
+        R, N = np64(ro), np64(no)
+        check_residual(R, ref, np64(inp.residual), "bf16")
+        check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")
+        nb = H // 16
+        same_blk = (N == ref.N).reshape(T, nb, 16).all(-1)
+        c_g = qo.reshape(T, nb, 8)
+        c_o = codes_or.reshape(T, nb, 8)
+        sf_g, sf_o = so[offs], sf_or[offs]
+        # blocks whose norm_out equals the oracle's: codes and scales bit-exact
+        assert np.array_equal(c_g[same_blk], c_o[same_blk])
+        assert np.array_equal(sf_g[same_blk], sf_o[same_blk])
+        assert same_blk.mean() > 0.98, same_blk.mean()
+        # other blocks (a 1-ulp norm_out difference): scale within one E4M3 step, codes within one
+        diff_sf = np.abs(sf_g.astype(int) - sf_o.astype(int))
+        assert diff_sf[~same_blk].max(initial=0) <= 1
+        # every byte outside the valid (t, b) scale positions is zero padding
+        if layout == 1:
+            pad = np.ones(so.size, bool)
+            pad[offs.ravel()] = False
+            assert not so[pad].any()
+        else:
+            assert so.size == T * nb
+        _say(f"  exact blocks {same_blk.mean():.5f} of {same_blk.size}")
+    # norm_out may be omitted: same codes
+    _, _, qo2, so2 = run_quant(inp, M.MOE_QUANT_NVFP4, gs, layout, with_norm=False)
+    assert np.array_equal(qo2, qo) and np.array_equal(so2, so)
+
+
+@pytest.mark.parametrize("T", [64, 3])
+def test_fp8(T):
+    inp = make_inputs(T, 6144, 8, seed=workload_seed("quant", T) + 7)
+    ref = oracle_ref(inp)
+    s8 = O.fp8_scale(ref.N)
+    codes_or = O.quant_fp8(ref.N, s8)
+    for use_ws in (True, False):
+        ro, no, qo, _ = run_quant(inp, M.MOE_QUANT_FP8_E4M3, s8, use_ws=use_ws)
+        R, N = np64(ro), np64(no)
+        check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")
+        same = N == ref.N
+        assert np.array_equal(qo[same], codes_or[same])
+        # elsewhere the code moves by at most one E4M3 step in the direction of the norm change
+        d = np.abs((qo[~same] & 0x7F).astype(int) - (codes_or[~same] & 0x7F).astype(int))
+        assert d.max(initial=0) <= 1
+        assert same.mean() > 0.99
+
+
+def test_quant_codec_edges():
+    """Saturation, tiny blocks (zero block scale) and signed zeros through the kernel: a row whose
+    values hit every E2M1 / E4M3 rounding midpoint exactly, built with dyadic inputs."""
+    T, H = 2, 1024
+    inp = _dyadic_inputs(T, H, 4, "bf16", seed=501)
+    ref = oracle_ref(inp)
+    for gs in (O.nvfp4_global_scale(ref.N), 1e-8, 3e4):
+        codes_or, sf_or = O.quant_nvfp4(ref.N, gs, 1)
+        ro, no, qo, so = run_quant(inp, M.MOE_QUANT_NVFP4, gs)
+        N = np64(no)
+        offs = _sf_offsets(T, H, 1)
+        same_blk = (N == ref.N).reshape(T, H // 16, 16).all(-1)
+        assert np.array_equal(qo.reshape(T, -1, 8)[same_blk], codes_or.reshape(T, -1, 8)[same_blk])
+        assert np.array_equal(so[offs][same_blk], sf_or[offs][same_blk])
+    for s8 in (O.fp8_scale(ref.N), 1e-6, 1e4):
+        codes_or = O.quant_fp8(ref.N, s8)
+        _, no, qo, _ = run_quant(inp, M.MOE_QUANT_FP8_E4M3, s8)
+        same = np64(no) == ref.N
+        assert np.array_equal(qo[same], codes_or[same])
