@@ -12,6 +12,7 @@
 namespace mfin {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -72,6 +73,16 @@ struct Act<ACT_FP16> {
     return r;
   }
 };
+
+// --- workgroup barrier for LDS traffic only ----------------------------------------------------
+// __syncthreads() also orders global memory, which makes every wavefront wait until its pending
+// global stores are acknowledged before the barrier. The kernels only exchange data through LDS,
+// so this barrier fences LDS alone and lets outstanding stores drain in the background.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // --- wavefront sum over DPP ---------------------------------------------------------------------
 // Sums v over the 64 lanes of a wavefront in a fixed order (so the result is bitwise

@@ -79,12 +79,23 @@ constexpr int kMaxSlices = 64;
 constexpr size_t kWsHeader = 256, kWsPerToken = 8 * kMaxSlices;
 constexpr uint32_t kMaxSpins = 1u << 22;      // ~0.1-0.5 s of polling, then give up (flagged)
 
+// Raw buffer resource over `bytes` bytes at `base` (gfx9-family descriptor word 3: 32-bit data
+// format, no swizzle). Loads outside [0, bytes) return zeros and stores there are dropped, so an
+// absent route, a missing optional tensor or a lane past the row needs no branch: its buffer is
+// empty or its offset is out of range.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
 // Partial sums of route groups g >= 1: [G-1][P][L] x 8 floats.
 extern __shared__ float4 lds_dyn[];
 
 template <int ACT, int MODE, int G, int P, int JMAX>
 __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
-  // blockIdx.x = token * slices + slice (one slice per token in the row modes)
+  // blockIdx.x = token * slices + slice (one slice per token in the whole-row modes)
   const int t = blockIdx.x / a.slices;
   const int slice = blockIdx.x - t * a.slices;
   const int tid = threadIdx.x;
@@ -92,56 +103,73 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   const int g = __builtin_amdgcn_readfirstlane(tid / L);   // wave-uniform route group
   const int lane = tid - g * L;
   const int slot0 = slice * a.slot_span;
+  const uint32_t row_bytes = (uint32_t)a.H * 2;
+  const int64_t tok_off = (int64_t)t * row_bytes;
 
-  // ---- route metadata: all K indices and scales of the token in one coalesced load per
-  // wavefront (lane k holds route k), issued before any row load. Routes are later read back
-  // with readlane, so their row addresses are wave-uniform (scalar base + lane offset).
-  const int lane64 = tid & 63;
-  int my_idx = -1;
-  float my_w = 0.f;
-  if (lane64 < a.K) {
-    const int64_t mk = (int64_t)t * a.K + lane64;
-    my_idx = a.idx[mk];
-    if (a.scales == nullptr) {
-      my_w = 1.f;
-    } else if (a.scales_bf16) {
-      my_w = Act<ACT_BF16>::scalar(((const uint16_t*)a.scales)[mk]);
-    } else {
-      my_w = ((const float*)a.scales)[mk];
-    }
-  }
-
-  // ---- this lane's slots ----
-  int slot[P];
+  // Byte offset of each of this lane's 16-byte slots in a row. Lanes past the row or past this
+  // workgroup's slice get an out-of-range offset: their buffer loads read zeros and their
+  // buffer stores are dropped, so no branch guards any memory access.
+  uint32_t voff[P];
   bool live[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
-    slot[p] = slot0 + lane + p * L;
-    live[p] = slot[p] < a.nv && (lane + p * L) < a.slot_span;
+    const int sl = slot0 + lane + p * L;
+    live[p] = sl < a.nv && (lane + p * L) < a.slot_span;
+    voff[p] = live[p] ? (uint32_t)sl * 16u : kOutOfRange;
   }
 
-  const int64_t row_bytes = (int64_t)a.H * 2;
+  // ---- route metadata: all K indices and scales of the token, one coalesced load per
+  // wavefront (lane k holds route k), issued before any row load; read back with readlane so
+  // every row address is wave-uniform.
+  const int lane64 = tid & 63;
+  const bool bf16_scales = a.scales_bf16 != 0;
+  const uint32_t my_idx = __builtin_amdgcn_raw_buffer_load_b32(
+      rsrc(a.idx + (int64_t)t * a.K, (uint32_t)a.K * 4u), (uint32_t)lane64 * 4u, 0, 0);
+  // Raw scale bits of both formats; the unused (or missing) one has an empty buffer. Loads are
+  // predicated by buffer size, never by branches: a branch join makes the compiler wait for
+  // every outstanding load before the row loads are issued.
+  const uint32_t my_w32 = __builtin_amdgcn_raw_buffer_load_b32(
+      rsrc((const uint8_t*)a.scales + (int64_t)t * a.K * 4,
+           (a.scales && !bf16_scales) ? (uint32_t)a.K * 4u : 0u),
+      (uint32_t)lane64 * 4u, 0, 0);
+  const uint32_t my_w16 = __builtin_amdgcn_raw_buffer_load_b16(
+      rsrc((const uint8_t*)a.scales + (int64_t)t * a.K * 2,
+           (a.scales && bf16_scales) ? (uint32_t)a.K * 2u : 0u),
+      (uint32_t)lane64 * 2u, 0, 0);
+  [[maybe_unused]] double qs = 0.0;
+  if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) qs = (double)*a.qscale;
+  // Split rows: this slice's current epoch word, read now so the barrier does not wait for it.
+  // Every wavefront reads it unconditionally (from gamma, a valid dummy, when rows are whole):
+  // a load under a branch would make the compiler wait for it at the branch join.
+  [[maybe_unused]] uint64_t epoch_word = 0;
+  if constexpr (MODE != MODE_FIN) {
+    const uint64_t* ep = a.slices > 1
+                             ? (const uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken) + slice
+                             : (const uint64_t*)a.gamma;
+    epoch_word = __hip_atomic_load(ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
-  // Group 0 also needs the shared-expert, residual and gamma slices; issue them up front.
+  // Group 0 also needs the shared-expert, residual and gamma slices; issue them alongside.
   u32x4 shv[P], resv[P], gamv[P];
+  {
+    const auto sh_r = rsrc(a.shared + tok_off, (g == 0 && a.shared) ? row_bytes : 0u);
 #pragma unroll
-  for (int p = 0; p < P; ++p) shv[p] = resv[p] = gamv[p] = (u32x4){0u, 0u, 0u, 0u};
-  if (g == 0) {
-    const int64_t tok_off = (int64_t)t * row_bytes;
+    for (int p = 0; p < P; ++p) shv[p] = __builtin_amdgcn_raw_buffer_load_b128(sh_r, voff[p], 0, 0);
+    if constexpr (MODE != MODE_FIN) {
+      const auto res_r = rsrc(a.residual + tok_off, g == 0 ? row_bytes : 0u);
+      const auto gam_r = rsrc(a.gamma, g == 0 ? row_bytes : 0u);
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      if (live[p]) {
-        if (a.shared) shv[p] = ((const u32x4*)(a.shared + tok_off))[slot[p]];
-        if (MODE != MODE_FIN) {
-          resv[p] = ((const u32x4*)(a.residual + tok_off))[slot[p]];
-          gamv[p] = ((const u32x4*)a.gamma)[slot[p]];
-        }
+      for (int p = 0; p < P; ++p) {
+        resv[p] = __builtin_amdgcn_raw_buffer_load_b128(res_r, voff[p], 0, 0);
+        gamv[p] = __builtin_amdgcn_raw_buffer_load_b128(gam_r, voff[p], 0, 0);
       }
     }
   }
 
-  // ---- row gather: per chunk of CH routes, issue every present route's 128-bit loads, then
-  // accumulate them in float32 (fused multiply-add) ----
+  // ---- row gather: per chunk of CH routes, issue every route's 128-bit loads (an absent
+  // route's buffer is empty and reads zeros), then accumulate the present ones in float32 ----
+  // exactly one of the two scale buffers is non-empty, the other reads zeros
+  const uint32_t my_wbits = my_w32 | (my_w16 << 16);
   constexpr int CH = JMAX < 16 / P ? JMAX : 16 / P;
   float acc[P][8];
 #pragma unroll
@@ -151,7 +179,6 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
 #pragma unroll
   for (int c0 = 0; c0 < JMAX; c0 += CH) {
     if (g + c0 * G >= a.K) break;
-    int pidx[CH];
     float w[CH];
     bool present[CH];
     u32x4 v[CH][P];
@@ -159,19 +186,20 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     for (int jj = 0; jj < CH; ++jj) {
       const int k = g + (c0 + jj) * G;
       const int kk = k < a.K ? k : 0;
-      pidx[jj] = __builtin_amdgcn_readlane(my_idx, kk);
-      w[jj] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), kk));
-      present[jj] = k < a.K && (uint64_t)(int64_t)pidx[jj] < (uint64_t)a.n_rows;
-      const u32x4* rowp = (const u32x4*)(a.rows + (int64_t)pidx[jj] * row_bytes);
+      const int pidx = __builtin_amdgcn_readlane((int)my_idx, kk);
+      present[jj] = k < a.K && (uint32_t)pidx < (uint32_t)a.n_rows;
+      const uint32_t wbits = (uint32_t)__builtin_amdgcn_readlane((int)my_wbits, kk);
+      // an absent route's scale is never used: its weight is 0 (and its row reads zeros)
+      w[jj] = present[jj] ? (a.scales ? __builtin_bit_cast(float, wbits) : 1.f) : 0.f;
+      // an absent route gets an empty buffer: its loads read zeros and touch no memory
+      const auto row_r = rsrc(a.rows + (int64_t)pidx * row_bytes, present[jj] ? row_bytes : 0u);
 #pragma unroll
-      for (int p = 0; p < P; ++p) {
-        v[jj][p] = (u32x4){0u, 0u, 0u, 0u};
-        if (present[jj] && live[p]) v[jj][p] = rowp[slot[p]];
-      }
+      for (int p = 0; p < P; ++p) v[jj][p] = __builtin_amdgcn_raw_buffer_load_b128(row_r, voff[p], 0, 0);
     }
+    // Every route is accumulated (an absent one adds 0 * 0): a use under a branch would let the
+    // compiler sink the load into it and serialize the row loads.
 #pragma unroll
     for (int jj = 0; jj < CH; ++jj) {
-      if (!present[jj]) continue;
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         float x[8];
@@ -192,7 +220,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
         dst[1] = make_float4(acc[p][4], acc[p][5], acc[p][6], acc[p][7]);
       }
     }
-    __syncthreads();
+    lds_barrier();
     if (g == 0) {
 #pragma unroll
       for (int gg = 1; gg < G; ++gg) {
@@ -209,9 +237,11 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
 
   // ---- routed scaling, shared add, the one rounding; then residual add ----
   float r[P][8];
+  u32x4 r_pk[P];
   float ss = 0.f;
   if (g == 0) {
-    const int64_t tok_off = (int64_t)t * row_bytes;
+    const auto fin_r = rsrc(a.out + tok_off, MODE == MODE_FIN ? row_bytes : 0u);
+    const auto ro_r = rsrc(a.residual_out + tok_off, a.residual_out ? row_bytes : 0u);
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       float sh[8];
@@ -221,20 +251,19 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
       for (int e = 0; e < 8; ++e) sv[e] = __builtin_fmaf(a.rsf, acc[p][e], sh[e]);
       const u32x4 s_pk = Act<ACT>::pack(sv);
       if constexpr (MODE == MODE_FIN) {
-        if (live[p]) ((u32x4*)(a.out + tok_off))[slot[p]] = s_pk;
+        __builtin_amdgcn_raw_buffer_store_b128(s_pk, fin_r, voff[p], 0, 0);
       } else {
         float s_r[8], res[8];
         Act<ACT>::unpack(s_pk, s_r);
         Act<ACT>::unpack(resv[p], res);
 #pragma unroll
         for (int e = 0; e < 8; ++e) r[p][e] = s_r[e] + res[e];
-        const u32x4 r_pk = Act<ACT>::pack(r[p]);
-        Act<ACT>::unpack(r_pk, r[p]);                 // keep the rounded residual_out
-        if (live[p]) {
-          if (a.residual_out) ((u32x4*)(a.residual_out + tok_off))[slot[p]] = r_pk;
+        r_pk[p] = Act<ACT>::pack(r[p]);
+        Act<ACT>::unpack(r_pk[p], r[p]);              // keep the rounded residual_out
+        __builtin_amdgcn_raw_buffer_store_b128(r_pk[p], ro_r, voff[p], 0, 0);
+        // lanes outside the row hold zeros here (all their loads read zeros)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(r[p][e], r[p][e], ss);
-        }
+        for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(r[p][e], r[p][e], ss);
       }
     }
   }
@@ -250,16 +279,14 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     const float ws = wave_sum(ss);
     if ((tid & 63) == 0) wave_part[wave] = ws;
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < 64) {                               // wavefront 0 of the workgroup
     float tot = 0.f;
     for (int i = 0; i < n_waves0; ++i) tot += wave_part[i];
     if (a.slices > 1) {
       uint64_t* slot = (uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken);
       const int S = a.slices;
-      const uint32_t epoch =
-          (uint32_t)(__hip_atomic_load(slot + slice, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >>
-                     32) + 1u;
+      const uint32_t epoch = (uint32_t)(epoch_word >> 32) + 1u;
       const int m = slice + tid * S;              // this slice's slots
       if (m < kMaxSlices) {
         const uint64_t v = ((uint64_t)epoch << 32) |
@@ -289,13 +316,14 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     }
     if (tid == 0) row_total = tot;
   }
-  __syncthreads();
+  lds_barrier();
   if (g != 0) return;
   const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(row_total, a.inv_h, a.eps));
 
-  const int64_t tok_off = (int64_t)t * row_bytes;
-  [[maybe_unused]] double qs = 0.0;
-  if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) qs = (double)*a.qscale;
+  const auto no_r = rsrc(a.out + tok_off, a.out ? row_bytes : 0u);
+  [[maybe_unused]] const uint32_t qrow = MODE == MODE_FP8 ? (uint32_t)a.H : (uint32_t)a.H / 2u;
+  [[maybe_unused]] const auto q_r =
+      rsrc(a.quant_out + (int64_t)t * qrow, (MODE == MODE_FP8 || MODE == MODE_NVFP4) ? qrow : 0u);
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     float gm[8], n[8];
@@ -303,21 +331,18 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) n[e] = (r[p][e] * rinv) * gm[e];
     const u32x4 n_pk = Act<ACT>::pack(n);
-    if (a.out && live[p]) ((u32x4*)(a.out + tok_off))[slot[p]] = n_pk;
+    __builtin_amdgcn_raw_buffer_store_b128(n_pk, no_r, voff[p], 0, 0);
     if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) {
       float nr[8];
       Act<ACT>::unpack(n_pk, nr);               // quantize the rounded norm_out values
       if constexpr (MODE == MODE_FP8) {
-        uint32_t lo = 0, hi = 0;
+        u32x2 q = {0u, 0u};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const uint32_t c = e4m3_code(__builtin_fabs((double)nr[e]) * qs) | (sign_bit(nr[e]) << 7);
-          if (e < 4) lo |= c << (8 * e); else hi |= c << (8 * (e - 4));
+          q[e >> 2] |= c << (8 * (e & 3));
         }
-        if (live[p]) {
-          uint2* q = (uint2*)(a.quant_out + (int64_t)t * a.H) + slot[p];
-          *q = make_uint2(lo, hi);
-        }
+        __builtin_amdgcn_raw_buffer_store_b64(q, q_r, voff[p] >> 1, 0, 0);
       } else {
         // NVFP4: 16-element block = this lane's 8 elements + the neighbouring lane's 8.
         float amax = 0.f;
@@ -333,14 +358,14 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
           if (sfc != 0) m = e2m1_code(__builtin_fabs((double)nr[e]) * qs, sf);
           word |= (m | (sign_bit(nr[e]) << 3)) << (4 * e);
         }
-        if (live[p]) ((uint32_t*)(a.quant_out + (int64_t)t * (a.H / 2)))[slot[p]] = word;
+        __builtin_amdgcn_raw_buffer_store_b32(word, q_r, voff[p] >> 2, 0, 0);
         // Scale bytes: lanes 8m..8m+7 hold blocks 4m'..4m'+3 (two lanes per block).
         const uint32_t sf_here = live[p] ? sfc : 0u;
         const uint32_t b1 = __shfl_down(sf_here, 2, 64);
         const uint32_t b2 = __shfl_down(sf_here, 4, 64);
         const uint32_t b3 = __shfl_down(sf_here, 6, 64);
-        const int s = slot[p];
-        if ((s & 7) == 0 && s < a.nv) {
+        const int s = slot0 + lane + p * L;
+        if (live[p] && (s & 7) == 0) {
           const int b = s >> 1;                  // first block of the group of four
           const int nb = a.H >> 4;
           const uint32_t packed = sf_here | (b1 << 8) | (b2 << 16) | (b3 << 24);
@@ -405,13 +430,15 @@ static void finish_config(int K, Config* c) {
   c->lds = (size_t)(G - 1) * c->P * c->L * 32;
 }
 
-// Slices per token for the split row modes: enough workgroups to put every CU to work
-// (about 1024 in total), each slice at least one wavefront of 8-element slots wide.
-// 1 = whole rows (no workspace needed).
+// Slices per token for the split row modes. A CU keeps only so many vector memory requests in
+// flight, so a whole row per workgroup leaves bandwidth unused when there are fewer tokens than
+// CUs; splitting costs one cross-workgroup exchange (~1 us). Measured on MI355X, the best count
+// gives about one workgroup per CU: min(slots / 64, 224 / T) (whole rows from T = 128 on), with
+// every slice at least one wavefront of 8-element slots wide. 1 = whole rows (no workspace).
 static int choose_slices(int64_t T, int nv) {
   const int max_by_h = nv / 64;
-  int want = (int)((1024 + T - 1) / T);
-  int S = want < max_by_h ? want : max_by_h;
+  int S = (int)(224 / (T > 0 ? T : 1));
+  if (S > max_by_h) S = max_by_h;
   if (S > kMaxSlices) S = kMaxSlices;
   for (; S > 1; --S) {
     const int span = ((nv + S - 1) / S + 7) / 8 * 8;
