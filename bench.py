@@ -15,6 +15,7 @@ finalize kernel, the FP64 CPU oracle's throughput on the host as a baseline).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import statistics
@@ -24,6 +25,33 @@ import time
 import numpy as np
 
 METRIC = "µs/call and achieved HBM GB/s (% of peak) for MoE finalize+RMSNorm, T=1..128"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = ["moe_expert_output_amd/csrc/finalize_kernels.hip",
+                  "moe_expert_output_amd/csrc/device_utils.h"]
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (two runs), scaled
+# by the same counters' reading for a plain copy of known size; valid only for the kernel
+# sources it was taken with.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_finalize_rmsnorm_T128_H7168_K8.json")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None if the kernel changed."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
 PEAK_GBS = 8000.0
 ACT_BYTES = 2
 
@@ -128,6 +156,10 @@ def main():
 
     # The pages' protocol (warm): one graph of 20 calls on the same inputs, median of 50 replays.
     warm = _warm_us(torch, stream, lambda: call(sets[0]))
+    # Context: a plain device copy moving the same number of bytes (half read, half written),
+    # rotated over the same amount of memory; also the known-size kernel that calibrates the
+    # FETCH_SIZE / WRITE_SIZE counters.
+    copy_us = _copy_reference(torch, stream, dev, nbytes, n_sets)
     floor = _warm_us(torch, stream, lambda: M.moe_finalize_launch_floor_run(1, T, H, K,
                                                                            device=dev))
     out = {
@@ -154,10 +186,11 @@ def main():
         "launch_floor_us": round(floor, 3),
         "algorithmic_bytes_per_call": nbytes,
         "host_wall_s": round(t_host1 - t_host0, 4),
+        "plain_copy_same_bytes_us": round(copy_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_GBS, 4), "traffic": None,
-                     "kernel": "mfin::finalize_kernel<bf16, RMS, G=1, P=1, JMAX=8>",
-                     "per_launch_bytes": nbytes},
+                     "frac": round(gbs / PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "kernel": "mfin::finalize_kernel<0, 1, 1, 1, 8> (bf16, RMSNorm, whole rows)",
+                     "per_launch_bytes": nbytes, "kernel_source_hash": kernel_source_hash()},
     }
     if a.sweep:
         out["cases"] = _sweep(torch, M, stream, dev, ws)
@@ -165,6 +198,31 @@ def main():
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, nbytes, a.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def _copy_reference(torch, stream, dev, nbytes, n_sets, replays=20):
+    half = nbytes // 2 // 2 * 2
+    srcs = [torch.empty(half // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+            for _ in range(n_sets)]
+    dsts = [torch.empty_like(x) for x in srcs]
+    with torch.cuda.stream(stream):
+        for s_, d_ in zip(srcs, dsts):
+            d_.copy_(s_)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for s_, d_ in zip(srcs, dsts):
+                d_.copy_(s_)
+        times = []
+        for _ in range(replays):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3 / n_sets)
+    return statistics.median(times)
 
 
 def _warm_us(torch, stream, fn, launches=20, replays=50):
