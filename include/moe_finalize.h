@@ -175,6 +175,23 @@ int moe_finalize_quant_run(const void* permuted_rows, int64_t num_permuted_rows,
 size_t moe_finalize_workspace_size(int64_t num_tokens, int64_t hidden, int top_k);
 
 /*
+ * moe_quantize_run -- NVFP4 or FP8-E4M3 quantization of a given [num_tokens, hidden] activation
+ * tensor x (act_dtype), with exactly the encoder of moe_finalize_quant_run (same definitions,
+ * layouts, rounding and saturation; see there). Applied to a precomputed norm_out it is the
+ * quantize step of [FI3385] walkthrough on its own (the standalone RMSNorm + quant pattern);
+ * it also lets a caller quantize values produced elsewhere.
+ *   x           [num_tokens, hidden] act_dtype, 16-byte aligned.
+ *   quant_scale device pointer to one float32 (gs for NVFP4, s8 for FP8).
+ *   quant_out   NVFP4 [num_tokens, hidden/2] bytes | FP8 [num_tokens, hidden] bytes.
+ *   scale_out   NVFP4: moe_finalize_sf_size(num_tokens, hidden, sf_layout) bytes (padding written
+ *               as 0); ignored for FP8.
+ * Errors as for moe_finalize_quant_run; hidden must be a multiple of 16 (NVFP4) or 8 (FP8).
+ */
+int moe_quantize_run(const void* x, int64_t num_tokens, int64_t hidden, int act_dtype,
+                     int quant_type, const float* quant_scale, void* quant_out, void* scale_out,
+                     int sf_layout, void* stream);
+
+/*
  * moe_finalize_sf_size -- bytes of the NVFP4 block-scale buffer for a [num_tokens, hidden]
  * output: SWIZZLED_128x4 pads rows to a multiple of 128 and blocks per row to a multiple of 4,
  * roundup(T,128) * roundup(H/16,4) ([FI6631] test changes: T*H/16 bytes is too small and was

@@ -22,7 +22,7 @@ MOE_SF_LINEAR, MOE_SF_SWIZZLED_128x4 = 0, 1
 # Every symbol include/moe_finalize.h declares.
 EXPORTED = ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_run",
             "moe_finalize_sf_size", "moe_finalize_error_string", "moe_finalize_version",
-            "moe_finalize_launch_floor_run", "moe_finalize_workspace_size")
+            "moe_finalize_launch_floor_run", "moe_finalize_workspace_size", "moe_quantize_run")
 
 _ACT = {torch.bfloat16: MOE_DTYPE_BF16, torch.float16: MOE_DTYPE_FP16}
 _SCALE = {torch.float32: MOE_DTYPE_FP32, torch.bfloat16: MOE_DTYPE_BF16}
@@ -47,6 +47,8 @@ def _load() -> ctypes.CDLL:
                                              vp, sz, i64, i64, i32, i32, vp]
     lib.moe_finalize_quant_run.argtypes = [vp, i64, vp, vp, i32, vp, f32, vp, vp, f32, i32, vp,
                                            vp, vp, i32, vp, vp, vp, sz, i64, i64, i32, i32, vp]
+    lib.moe_quantize_run.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, i32, vp]
+    lib.moe_quantize_run.restype = ctypes.c_int
     lib.moe_finalize_workspace_size.argtypes = [i64, i64, i32]
     lib.moe_finalize_workspace_size.restype = sz
     for f in ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_run"):
@@ -172,3 +174,14 @@ def moe_finalize_quant_run(permuted_rows: torch.Tensor, expanded_idx_to_permuted
         _ptr(residual), _ptr(gamma), float(eps), int(quant_type), _ptr(quant_scale),
         _ptr(quant_out), _ptr(scale_out), int(sf_layout), _ptr(residual_out), _ptr(norm_out),
         wp, wb, T, H, K, act, _stream(residual, stream)))
+
+
+def moe_quantize_run(x: torch.Tensor, quant_type: int, quant_scale: torch.Tensor,
+                     quant_out: torch.Tensor, scale_out: Optional[torch.Tensor], sf_layout: int,
+                     stream=None) -> None:
+    if x.dtype not in _ACT:
+        raise ValueError(f"activation dtype {x.dtype} is not bf16/fp16")
+    T, H = x.shape
+    _check(LIB.moe_quantize_run(_ptr(x), T, H, _ACT[x.dtype], int(quant_type), _ptr(quant_scale),
+                                _ptr(quant_out), _ptr(scale_out), int(sf_layout),
+                                _stream(x, stream)))

@@ -93,6 +93,86 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 // Partial sums of route groups g >= 1: [G-1][P][L] x 8 floats.
 extern __shared__ float4 lds_dyn[];
 
+// Where quantized outputs go (shared by the fused epilogue and the standalone quantizer).
+struct QuantDst {
+  uint8_t* sf_out;    // NVFP4 block scales
+  int H;
+  int sf_swizzled;
+};
+
+// Quantize the 8 rounded values `nr` of slot `s` of row `t` (this lane) and store the codes
+// through `q_r` (the row's code buffer); for NVFP4 also the block scales. Every lane of the
+// wavefront must call it (the NVFP4 block amax and scale gathers are cross-lane). Lanes with
+// live == false hold zeros and store nothing.
+template <int MODE>
+__device__ __forceinline__ void quantize_store(const float nr[8], double qs,
+                                               const __amdgpu_buffer_rsrc_t& q_r, uint32_t voff,
+                                               bool live, int s, int t, const QuantDst& d) {
+  if constexpr (MODE == MODE_FP8) {
+    u32x2 q = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t c = e4m3_code(__builtin_fabs((double)nr[e]) * qs) | (sign_bit(nr[e]) << 7);
+      q[e >> 2] |= c << (8 * (e & 3));
+    }
+    __builtin_amdgcn_raw_buffer_store_b64(q, q_r, voff >> 1, 0, 0);
+  } else {
+    // NVFP4: a 16-element block is this lane's 8 elements and the neighbouring lane's 8.
+    float amax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, __builtin_fabsf(nr[e]));
+    amax = pair_max(amax);
+    const uint32_t sfc = e4m3_code((double)amax * qs / 6.0);
+    const double sf = e4m3_value(sfc);
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint32_t m = 0;
+      if (sfc != 0) m = e2m1_code(__builtin_fabs((double)nr[e]) * qs, sf);
+      word |= (m | (sign_bit(nr[e]) << 3)) << (4 * e);
+    }
+    __builtin_amdgcn_raw_buffer_store_b32(word, q_r, voff >> 2, 0, 0);
+    // Scale bytes: lanes 8m..8m+7 hold blocks 4m'..4m'+3 (two lanes per block).
+    const uint32_t sf_here = live ? sfc : 0u;
+    const uint32_t b1 = __shfl_down(sf_here, 2, 64);
+    const uint32_t b2 = __shfl_down(sf_here, 4, 64);
+    const uint32_t b3 = __shfl_down(sf_here, 6, 64);
+    if (live && (s & 7) == 0) {
+      const int b = s >> 1;                      // first block of the group of four
+      const int nb = d.H >> 4;
+      const uint32_t packed = sf_here | (b1 << 8) | (b2 << 16) | (b3 << 24);
+      if (d.sf_swizzled) {
+        const int nb4 = (nb + 3) & ~3;
+        const int64_t off = ((int64_t)(t >> 7) * (nb4 >> 2) + (b >> 2)) * 512 + (t & 31) * 16 +
+                            ((t & 127) >> 5) * 4;
+        *(uint32_t*)(d.sf_out + off) = packed;   // padding blocks carry sf 0
+      } else {
+        uint8_t* dst = d.sf_out + (int64_t)t * nb + b;
+        const uint8_t bytes[4] = {(uint8_t)sf_here, (uint8_t)b1, (uint8_t)b2, (uint8_t)b3};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (b + i < nb) dst[i] = bytes[i];
+      }
+    }
+  }
+}
+
+// Zero the swizzled scale rows between T and the next multiple of 128: row t's workgroup takes
+// rows T + t, T + t + T, ...; its `nthreads` threads split each row's 32-bit words.
+__device__ __forceinline__ void zero_sf_padding(const QuantDst& d, int T, int t, int tid,
+                                                int nthreads) {
+  const int nb4 = ((d.H >> 4) + 3) & ~3;
+  const int words = nb4 >> 2;
+  const int t_pad_end = (T + 127) & ~127;
+  for (int rr = T + t; rr < t_pad_end; rr += T) {
+    for (int i = tid; i < words; i += nthreads) {
+      const int64_t off =
+          ((int64_t)(rr >> 7) * words + i) * 512 + (rr & 31) * 16 + ((rr & 127) >> 5) * 4;
+      *(uint32_t*)(d.sf_out + off) = 0u;
+    }
+  }
+}
+
 template <int ACT, int MODE, int G, int P, int JMAX>
 __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   // blockIdx.x = token * slices + slice (one slice per token in the whole-row modes)
@@ -335,71 +415,44 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) {
       float nr[8];
       Act<ACT>::unpack(n_pk, nr);               // quantize the rounded norm_out values
-      if constexpr (MODE == MODE_FP8) {
-        u32x2 q = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t c = e4m3_code(__builtin_fabs((double)nr[e]) * qs) | (sign_bit(nr[e]) << 7);
-          q[e >> 2] |= c << (8 * (e & 3));
-        }
-        __builtin_amdgcn_raw_buffer_store_b64(q, q_r, voff[p] >> 1, 0, 0);
-      } else {
-        // NVFP4: 16-element block = this lane's 8 elements + the neighbouring lane's 8.
-        float amax = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, __builtin_fabsf(nr[e]));
-        amax = pair_max(amax);
-        const uint32_t sfc = e4m3_code((double)amax * qs / 6.0);
-        const double sf = e4m3_value(sfc);
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint32_t m = 0;
-          if (sfc != 0) m = e2m1_code(__builtin_fabs((double)nr[e]) * qs, sf);
-          word |= (m | (sign_bit(nr[e]) << 3)) << (4 * e);
-        }
-        __builtin_amdgcn_raw_buffer_store_b32(word, q_r, voff[p] >> 2, 0, 0);
-        // Scale bytes: lanes 8m..8m+7 hold blocks 4m'..4m'+3 (two lanes per block).
-        const uint32_t sf_here = live[p] ? sfc : 0u;
-        const uint32_t b1 = __shfl_down(sf_here, 2, 64);
-        const uint32_t b2 = __shfl_down(sf_here, 4, 64);
-        const uint32_t b3 = __shfl_down(sf_here, 6, 64);
-        const int s = slot0 + lane + p * L;
-        if (live[p] && (s & 7) == 0) {
-          const int b = s >> 1;                  // first block of the group of four
-          const int nb = a.H >> 4;
-          const uint32_t packed = sf_here | (b1 << 8) | (b2 << 16) | (b3 << 24);
-          if (a.sf_swizzled) {
-            const int nb4 = (nb + 3) & ~3;
-            const int64_t off = ((int64_t)(t >> 7) * (nb4 >> 2) + (b >> 2)) * 512 +
-                                (t & 31) * 16 + ((t & 127) >> 5) * 4;
-            *(uint32_t*)(a.sf_out + off) = packed;   // padding blocks carry sf 0
-          } else {
-            uint8_t* dst = a.sf_out + (int64_t)t * nb + b;
-            const uint8_t bytes[4] = {(uint8_t)sf_here, (uint8_t)b1, (uint8_t)b2, (uint8_t)b3};
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (b + i < nb) dst[i] = bytes[i];
-          }
-        }
-      }
+      quantize_store<MODE>(nr, qs, q_r, voff[p], live[p], slot0 + lane + p * L, t,
+                           QuantDst{a.sf_out, a.H, a.sf_swizzled});
     }
   }
-
-  // Zero the swizzled scale rows between T and the next multiple of 128, spread over tokens.
   if constexpr (MODE == MODE_NVFP4) {
-    if (a.sf_swizzled && slice == 0) {
-      const int nb4 = ((a.H >> 4) + 3) & ~3;
-      const int words = nb4 >> 2;
-      const int t_pad_end = (a.T + 127) & ~127;
-      for (int rr = a.T + t; rr < t_pad_end; rr += a.T) {
-        for (int i = tid; i < words; i += L) {
-          const int64_t off = ((int64_t)(rr >> 7) * words + i) * 512 + (rr & 31) * 16 +
-                              ((rr & 127) >> 5) * 4;
-          *(uint32_t*)(a.sf_out + off) = 0u;
-        }
-      }
-    }
+    if (a.sf_swizzled && slice == 0) zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T, t, tid, L);
+  }
+}
+
+// Standalone quantizer: NVFP4 / FP8 of a given [T, H] activation tensor with the same device
+// code as the fused epilogue. One wavefront per token and 512-element slice.
+struct QuantParams {
+  const uint8_t* x;
+  const float* qscale;
+  uint8_t* quant_out;
+  uint8_t* sf_out;
+  int T, H, nv, slices, sf_swizzled;
+};
+
+template <int ACT, int MODE>
+__global__ __launch_bounds__(64) void quantize_kernel(const QuantParams a) {
+  const int t = blockIdx.x / a.slices;
+  const int slice = blockIdx.x - t * a.slices;
+  const int lane = threadIdx.x;
+  const int s = slice * 64 + lane;
+  const bool live = s < a.nv;
+  const uint32_t voff = live ? (uint32_t)s * 16u : kOutOfRange;
+  const uint32_t row_bytes = (uint32_t)a.H * 2u;
+  const double qs = (double)*a.qscale;
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc(a.x + (int64_t)t * row_bytes, row_bytes),
+                                                        voff, 0, 0);
+  float xr[8];
+  Act<ACT>::unpack(v, xr);
+  const uint32_t qrow = MODE == MODE_FP8 ? (uint32_t)a.H : (uint32_t)a.H / 2u;
+  const QuantDst d{a.sf_out, a.H, a.sf_swizzled};
+  quantize_store<MODE>(xr, qs, rsrc(a.quant_out + (int64_t)t * qrow, qrow), voff, live, s, t, d);
+  if constexpr (MODE == MODE_NVFP4) {
+    if (a.sf_swizzled && slice == 0) zero_sf_padding(d, a.T, t, lane, 64);
   }
 }
 
@@ -781,6 +834,54 @@ int moe_finalize_rmsnorm_run(const void* permuted_rows, int64_t num_permuted_row
     return rc;
   return run_rows(MODE_RMS, c, residual, gamma, eps, residual_out, norm_out, nullptr, nullptr,
                   nullptr, 0, workspace, stream);
+}
+
+int moe_quantize_run(const void* x, int64_t num_tokens, int64_t hidden, int act_dtype,
+                     int quant_type, const float* quant_scale, void* quant_out, void* scale_out,
+                     int sf_layout, void* stream) {
+  if (act_dtype != MOE_DTYPE_BF16 && act_dtype != MOE_DTYPE_FP16) return MOE_FIN_ERR_DTYPE;
+  if (quant_type != MOE_QUANT_NVFP4 && quant_type != MOE_QUANT_FP8_E4M3)
+    return MOE_FIN_ERR_QUANT_TYPE;
+  const bool nvfp4 = quant_type == MOE_QUANT_NVFP4;
+  if (nvfp4 && sf_layout != MOE_SF_LINEAR && sf_layout != MOE_SF_SWIZZLED_128x4)
+    return MOE_FIN_ERR_SF_LAYOUT;
+  if (hidden <= 0 || hidden % (nvfp4 ? 16 : 8) != 0 || hidden > ((int64_t)1 << 20))
+    return MOE_FIN_ERR_HIDDEN;
+  if (num_tokens < 0 || num_tokens > INT32_MAX / 2) return MOE_FIN_ERR_BAD_SHAPE;
+  if (num_tokens == 0) return MOE_FIN_OK;
+  if (!x || !quant_scale || !quant_out || (nvfp4 && !scale_out)) return MOE_FIN_ERR_NULL_POINTER;
+  if (!aligned(x, 16) || !aligned(quant_scale, 4) || !aligned(quant_out, 16) ||
+      (nvfp4 && !aligned(scale_out, 4)))
+    return MOE_FIN_ERR_ALIGNMENT;
+  const size_t xb = (size_t)num_tokens * hidden * 2;
+  const Range q = rng(quant_out, (size_t)num_tokens * hidden / (nvfp4 ? 2 : 1));
+  if (overlap(q, rng(x, xb)) || overlap(q, rng(quant_scale, 4))) return MOE_FIN_ERR_ALIAS;
+  if (nvfp4) {
+    const Range sr = rng(scale_out, moe_finalize_sf_size(num_tokens, hidden, sf_layout));
+    if (overlap(sr, rng(x, xb)) || overlap(sr, q) || overlap(sr, rng(quant_scale, 4)))
+      return MOE_FIN_ERR_ALIAS;
+  }
+  QuantParams p;
+  p.x = (const uint8_t*)x;
+  p.qscale = quant_scale;
+  p.quant_out = (uint8_t*)quant_out;
+  p.sf_out = (uint8_t*)scale_out;
+  p.T = (int)num_tokens;
+  p.H = (int)hidden;
+  p.nv = (int)(hidden / 8);
+  p.slices = (p.nv + 63) / 64;
+  p.sf_swizzled = sf_layout == MOE_SF_SWIZZLED_128x4;
+  if ((int64_t)p.slices * num_tokens > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
+  const dim3 grid((unsigned)(p.slices * num_tokens)), block(64);
+  hipStream_t s = (hipStream_t)stream;
+  if (act_dtype == MOE_DTYPE_BF16) {
+    if (nvfp4) hipLaunchKernelGGL((quantize_kernel<ACT_BF16, MODE_NVFP4>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((quantize_kernel<ACT_BF16, MODE_FP8>), grid, block, 0, s, p);
+  } else {
+    if (nvfp4) hipLaunchKernelGGL((quantize_kernel<ACT_FP16, MODE_NVFP4>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((quantize_kernel<ACT_FP16, MODE_FP8>), grid, block, 0, s, p);
+  }
+  return to_code(hipGetLastError());
 }
 
 int moe_finalize_quant_run(const void* permuted_rows, int64_t num_permuted_rows,

@@ -137,3 +137,19 @@ def test_quant_validation_codes():
     assert quant(qo=E + 0x400008) == -5
     assert quant(so=A) == -9
     assert quant(T=0) == 0
+
+
+def test_quantize_validation_codes():
+    q = LIB.moe_quantize_run
+    X, QS, QO, SO = A, E + 0x300000, E + 0x400000, E + 0x500000
+    assert q(X, 4, 1024, 0, 3, QS, QO, SO, 1, None) == -7
+    assert q(X, 4, 1024, 0, 1, QS, QO, SO, 2, None) == -8
+    assert q(X, 4, 1024, 9, 1, QS, QO, SO, 1, None) == -6
+    assert q(X, 4, 1032, 0, 1, QS, QO, SO, 1, None) == -4      # NVFP4 needs hidden % 16 == 0
+    assert q(X, 4, 1020, 0, 2, QS, QO, None, 0, None) == -4    # FP8 needs hidden % 8 == 0
+    assert q(X, -1, 1024, 0, 1, QS, QO, SO, 1, None) == -2
+    assert q(X, 0, 1024, 0, 1, None, None, None, 1, None) == 0
+    assert q(None, 4, 1024, 0, 1, QS, QO, SO, 1, None) == -1
+    assert q(X, 4, 1024, 0, 1, QS, QO, None, 1, None) == -1
+    assert q(X + 8, 4, 1024, 0, 1, QS, QO, SO, 1, None) == -5
+    assert q(X, 4, 1024, 0, 1, QS, X + 1024, SO, 1, None) == -9

@@ -411,3 +411,76 @@ def test_quant_codec_edges():
         _, no, qo, _ = run_quant(inp, M.MOE_QUANT_FP8_E4M3, s8)
         same = np64(no) == ref.N
         assert np.array_equal(qo[same], codes_or[same])
+
+
+# ---- quantizing the oracle's rounded values: bit-exact everywhere ------------------------------
+def _quantize_dev(N_vals, act, qtype, qscale, layout):
+    T, H = N_vals.shape
+    x = torch.from_numpy(N_vals.astype(np.float32)).to(ACT_T[act]).cuda()   # exact: N is act-valued
+    nv = qtype == M.MOE_QUANT_NVFP4
+    qo = torch.full((T, H // 2 if nv else H), 0xAB, dtype=torch.uint8, device="cuda")
+    so = None
+    if nv:
+        so = torch.full((M.moe_finalize_sf_size(T, H, layout),), 0xCD, dtype=torch.uint8,
+                        device="cuda")
+    qs = torch.tensor([qscale], dtype=torch.float32, device="cuda")
+    M.moe_quantize_run(x, qtype, qs, qo, so, layout)
+    torch.cuda.synchronize()
+    return qo.cpu().numpy(), (None if so is None else so.cpu().numpy())
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+@pytest.mark.parametrize("TH", [(64, 6144), (130, 2048), (3, 48), (1, 7168)])
+def test_quantize_oracle_values_bit_exact(TH, act):
+    T, H = TH
+    inp = make_inputs(T, H, 8, act_dtype=act, seed=workload_seed("quant", T, act) + H + 1)
+    N = oracle_ref(inp).N
+    N[0, :16] = 0.0                         # an all-zero block (scale 0)
+    N[-1, 16:32] = -N[-1, 16:32]
+    for layout in (M.MOE_SF_SWIZZLED_128x4, M.MOE_SF_LINEAR):
+        for gs in (O.nvfp4_global_scale(N), 1e-6, 5e3):
+            want_c, want_s = O.quant_nvfp4(N, gs, layout)
+            got_c, got_s = _quantize_dev(N, act, M.MOE_QUANT_NVFP4, gs, layout)
+            assert np.array_equal(got_c, want_c), (layout, gs)
+            assert np.array_equal(got_s, want_s), (layout, gs)
+    for s8 in (O.fp8_scale(N), 1e-3, 1e3):
+        want = O.quant_fp8(N, s8)
+        got, _ = _quantize_dev(N, act, M.MOE_QUANT_FP8_E4M3, s8, 0)
+        assert np.array_equal(got, want), s8
+
+
+def test_quantize_rounding_midpoints_bit_exact():
+    """Values placed exactly on E2M1 / E4M3 rounding midpoints (and one bf16 step either side),
+    so every tie-to-even decision of the encoders is exercised."""
+    gs = 1.0
+    # block scale 1.0 needs amax = 6: put 6.0 first in every block, then midpoints
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = []
+    for m in mids:
+        b = O.round_to_format(np.array([m]), O.BF16)[0]
+        up = float(np.nextafter(np.float32(b), np.float32(10)).astype(np.float32))
+        vals += [b, O.round_to_format(np.array([b * (1 + 2 ** -7)]), O.BF16)[0],
+                 O.round_to_format(np.array([b * (1 - 2 ** -8)]), O.BF16)[0], -b]
+    vals = np.array(vals)
+    n_blocks = (len(vals) + 14) // 15
+    row = np.zeros(n_blocks * 16)
+    for i in range(n_blocks):
+        row[16 * i] = 6.0
+        chunk = vals[15 * i:15 * i + 15]
+        row[16 * i + 1:16 * i + 1 + len(chunk)] = chunk
+    H = ((len(row) + 63) // 64) * 64
+    N = np.zeros((2, H))
+    N[0, :len(row)] = row
+    N[1, :len(row)] = row * 2.0 ** -5        # scale 6*2^-5/6: an E4M3 value
+    want_c, want_s = O.quant_nvfp4(N, gs, 1)
+    got_c, got_s = _quantize_dev(N, "bf16", M.MOE_QUANT_NVFP4, gs, 1)
+    assert np.array_equal(got_c, want_c) and np.array_equal(got_s, want_s)
+    # FP8: E4M3 midpoints in every binade
+    e4 = O.decode_bits(np.arange(0x7E, dtype=np.uint8), O.E4M3)
+    m8 = (e4[:-1] + e4[1:]) / 2
+    x = O.round_to_format(np.concatenate([m8, -m8, e4]), O.BF16)
+    H8 = ((len(x) + 7) // 8) * 8
+    N8 = np.zeros((1, H8))
+    N8[0, :len(x)] = x
+    assert np.array_equal(_quantize_dev(N8, "bf16", M.MOE_QUANT_FP8_E4M3, 1.0, 0)[0],
+                          O.quant_fp8(N8, 1.0))
