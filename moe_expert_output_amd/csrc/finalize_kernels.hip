@@ -512,9 +512,12 @@ static int choose_slices(int64_t T, int nv) {
   return S < 1 ? 1 : S;
 }
 
-// Finalize-only: one workgroup per token and 64-slot slice. Row modes: one workgroup per token
-// and slice (slices = 1 covers the whole row with P slots per lane).
-static bool make_config(int mode, int H, int K, int slices, Config* c) {
+// Finalize-only: one workgroup per token and 64-slot slice, with route groups chosen so each
+// wavefront keeps at least 4 routes in flight and the grid stays near 2048 wavefronts (measured
+// best on MI355X: G = 2 at K = 8 for small batches, G = 1 from T = 128, G = 4 at K >= 16 on
+// small grids). Row modes: one workgroup per token and slice (slices = 1 covers the whole row
+// with P slots per lane), with as many route groups as fit in 1024 lanes.
+static bool make_config(int mode, int64_t T, int H, int K, int slices, Config* c) {
   const int nv = H / 8;
   c->nontemporal = false;
   if (mode == MODE_FIN) {
@@ -522,7 +525,17 @@ static bool make_config(int mode, int H, int K, int slices, Config* c) {
     c->L = 64;
     c->span = 64;
     c->grid_x = (nv + 63) / 64;
-  } else if (slices > 1) {
+    int g_by_k = K >= 16 ? 4 : (K >= 8 ? 2 : 1);
+    const int64_t waves = (T > 0 ? T : 1) * c->grid_x;
+    int G = 1;
+    while (G < g_by_k && waves * 2 * G <= 2048) G *= 2;
+    c->G = G;
+    const int J = (K + G - 1) / G;
+    c->JMAX = next_pow2(J < 4 ? 4 : J);
+    c->lds = (size_t)(G - 1) * c->P * c->L * 32;
+    return true;
+  }
+  if (slices > 1) {
     c->P = 1;
     c->span = ((nv + slices - 1) / slices + 7) / 8 * 8;
     c->L = (c->span + 63) / 64 * 64;
@@ -674,7 +687,7 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
                     void* stream) {
   const int slices = workspace ? choose_slices(c.T, (int)(c.H / 8)) : 1;
   Config cfg;
-  if (!make_config(mode, (int)c.H, c.K, slices, &cfg)) return MOE_FIN_ERR_HIDDEN;
+  if (!make_config(mode, c.T, (int)c.H, c.K, slices, &cfg)) return MOE_FIN_ERR_HIDDEN;
   cfg.nontemporal = use_nontemporal(c.T, c.H, c.K);
   if ((int64_t)cfg.grid_x * c.T > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
   Params p = base_params(c);
@@ -791,7 +804,7 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
   if (num_tokens < 0 || num_tokens > INT32_MAX / 2) return MOE_FIN_ERR_BAD_SHAPE;
   if (num_tokens == 0) return MOE_FIN_OK;
   Config c;
-  make_config(entry == 0 ? MODE_FIN : MODE_RMS, (int)hidden, top_k,
+  make_config(entry == 0 ? MODE_FIN : MODE_RMS, num_tokens, (int)hidden, top_k,
               entry == 0 ? 1 : choose_slices(num_tokens, (int)(hidden / 8)), &c);
   if ((int64_t)c.grid_x * num_tokens > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(launch_floor_kernel, dim3((unsigned)(c.grid_x * num_tokens)), dim3(c.G * c.L),
@@ -815,7 +828,7 @@ int moe_finalize_run(const void* permuted_rows, int64_t num_permuted_rows,
   if (!aligned(out, 16)) return MOE_FIN_ERR_ALIGNMENT;
   if (inputs_overlap(c, rng(out, (size_t)num_tokens * hidden * 2))) return MOE_FIN_ERR_ALIAS;
   Config cfg;
-  make_config(MODE_FIN, (int)hidden, top_k, 1, &cfg);
+  make_config(MODE_FIN, num_tokens, (int)hidden, top_k, 1, &cfg);
   cfg.nontemporal = use_nontemporal(num_tokens, hidden, top_k);
   if ((int64_t)cfg.grid_x * num_tokens > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
   Params p = base_params(c);

@@ -484,3 +484,10 @@ def test_quantize_rounding_midpoints_bit_exact():
     N8[0, :len(x)] = x
     assert np.array_equal(_quantize_dev(N8, "bf16", M.MOE_QUANT_FP8_E4M3, 1.0, 0)[0],
                           O.quant_fp8(N8, 1.0))
+
+
+# ---- large batches (prefill-sized calls: whole rows, nontemporal streaming) ---------------------
+@pytest.mark.parametrize("THK", [(256, 7168, 8), (512, 7168, 8), (2048, 2048, 8), (300, 3584, 16)])
+def test_large_batch(THK):
+    T, H, K = THK
+    full_check(make_inputs(T, H, K, seed=5000 + T + K))
