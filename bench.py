@@ -10,7 +10,9 @@ HIP graph and replayed; HIP events on the launch stream bracket exactly K calls.
 Output: one JSON line (metric, value = achieved algorithmic GB/s, us/call, roofline of the
 finalize kernel, the FP64 CPU oracle's throughput on the host as a baseline).
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu-baseline]
---sweep adds µs/call (warm, cold, launch floor) for every decode shape of the pages' workloads.
+--sweep adds warm µs/call and the launch floor for every decode shape of the pages' workloads,
+and, for the hidden 1024/6144/7168 shapes, the unfused alternative (moe_finalize_run, then
+moe_residual_rmsnorm_run) beside the fused call.
 """
 from __future__ import annotations
 
@@ -265,22 +267,40 @@ def _sweep(torch, M, stream, dev, ws_big):
         ro = torch.empty(T, H, dtype=dt, device=dev)
         no = torch.empty(T, H, dtype=dt, device=dev)
         ws = ws_big
-        for entry in ("rmsnorm", "finalize"):
+        s_buf = torch.empty(T, H, dtype=dt, device=dev)
+        for entry in ("rmsnorm", "finalize", "two_kernel"):
             if entry == "finalize" and grp not in ("highk",):
                 continue
-            if entry == "rmsnorm":
+            if entry == "two_kernel" and grp not in ("tiny", "decode", "larger"):
+                continue
+            if entry == "two_kernel":
+                # the unfused alternative: finalize, then residual + RMSNorm as its own kernel
+                def fn(d=d, ro=ro, no=no, inp=inp, ws=ws, s_buf=s_buf):
+                    M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                       s_buf)
+                    M.moe_residual_rmsnorm_run(s_buf, d["residual"], d["gamma"], inp.eps, ro, no,
+                                               ws)
+
+                def floor_fn(T=T, H=H, K=K):               # two empty launches
+                    M.moe_finalize_launch_floor_run(0, T, H, K, device=dev)
+                    M.moe_finalize_launch_floor_run(1, T, H, 1, device=dev)
+            elif entry == "rmsnorm":
                 fn = (lambda d=d, ro=ro, no=no, inp=inp, ws=ws: M.moe_finalize_rmsnorm_run(
                     d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf, d["residual"],
                     d["gamma"], inp.eps, ro, no, ws))
-                fl = 1
+                floor_fn = (lambda T=T, H=H, K=K:
+                            M.moe_finalize_launch_floor_run(1, T, H, K, device=dev))
             else:
                 fn = (lambda d=d, no=no, inp=inp: M.moe_finalize_run(
                     d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf, no))
-                fl = 0
+                floor_fn = (lambda T=T, H=H, K=K:
+                            M.moe_finalize_launch_floor_run(0, T, H, K, device=dev))
             us = _warm_us(torch, stream, fn)
-            floor = _warm_us(torch, stream, lambda fl=fl, T=T, H=H, K=K:
-                             M.moe_finalize_launch_floor_run(fl, T, H, K, device=dev))
-            nb = algorithmic_bytes(T, H, K, n_valid, 4 if sdt == "fp32" else 2, sh, entry)
+            floor = _warm_us(torch, stream, floor_fn)
+            # the fused path's algorithmic bytes for both rmsnorm entries: the two-kernel
+            # path's extra write and re-read of s is the cost the fusion removes
+            nb = algorithmic_bytes(T, H, K, n_valid, 4 if sdt == "fp32" else 2, sh,
+                                   "rmsnorm" if entry == "two_kernel" else entry)
             cases.append({"group": grp, "entry": entry, "T": T, "H": H, "K": K, "act": act,
                           "scales": sdt, "us_warm": round(us, 3), "floor_us": round(floor, 3),
                           "excess_us": round(us - floor, 3), "bytes": nb,

@@ -192,6 +192,26 @@ int moe_quantize_run(const void* x, int64_t num_tokens, int64_t hidden, int act_
                      int sf_layout, void* stream);
 
 /*
+ * moe_residual_rmsnorm_run -- the residual add and RMSNorm of moe_finalize_rmsnorm_run on a given
+ * activation x instead of a finalize result: r = RNE_T(x + residual), norm = RNE_T(r * gamma /
+ * sqrt(mean_h(r^2) + eps)). This is the separate residual + RMSNorm kernel that the fused
+ * finalize is measured against ([FI6631] Related Issues: fused finalize versus finalize
+ * followed by a residual + RMSNorm kernel) and the residual + RMSNorm stage of an all-reduce
+ * fusion ([FI3385] Description). Runs on the finalize kernel with one route per token (row t of
+ * x, weight 1), routed scaling 1 and no shared term, which reproduces x exactly.
+ *
+ *   x             [num_tokens, hidden] act_dtype, 16-byte aligned.
+ *   residual, gamma, eps, residual_out, norm_out, workspace, workspace_bytes
+ *                 as in moe_finalize_rmsnorm_run (residual_out may equal residual; it may not
+ *                 overlap x).
+ * Errors as for moe_finalize_rmsnorm_run (top_k checks do not apply).
+ */
+int moe_residual_rmsnorm_run(const void* x, const void* residual, const void* gamma, float eps,
+                             void* residual_out, void* norm_out,
+                             void* workspace, size_t workspace_bytes,
+                             int64_t num_tokens, int64_t hidden, int act_dtype, void* stream);
+
+/*
  * moe_finalize_sf_size -- bytes of the NVFP4 block-scale buffer for a [num_tokens, hidden]
  * output: SWIZZLED_128x4 pads rows to a multiple of 128 and blocks per row to a multiple of 4,
  * roundup(T,128) * roundup(H/16,4) ([FI6631] test changes: T*H/16 bytes is too small and was

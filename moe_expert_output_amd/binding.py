@@ -22,7 +22,8 @@ MOE_SF_LINEAR, MOE_SF_SWIZZLED_128x4 = 0, 1
 # Every symbol include/moe_finalize.h declares.
 EXPORTED = ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_run",
             "moe_finalize_sf_size", "moe_finalize_error_string", "moe_finalize_version",
-            "moe_finalize_launch_floor_run", "moe_finalize_workspace_size", "moe_quantize_run")
+            "moe_finalize_launch_floor_run", "moe_finalize_workspace_size", "moe_quantize_run",
+            "moe_residual_rmsnorm_run")
 
 _ACT = {torch.bfloat16: MOE_DTYPE_BF16, torch.float16: MOE_DTYPE_FP16}
 _SCALE = {torch.float32: MOE_DTYPE_FP32, torch.bfloat16: MOE_DTYPE_BF16}
@@ -49,6 +50,8 @@ def _load() -> ctypes.CDLL:
                                            vp, vp, i32, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.moe_quantize_run.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, i32, vp]
     lib.moe_quantize_run.restype = ctypes.c_int
+    lib.moe_residual_rmsnorm_run.argtypes = [vp, vp, vp, f32, vp, vp, vp, sz, i64, i64, i32, vp]
+    lib.moe_residual_rmsnorm_run.restype = ctypes.c_int
     lib.moe_finalize_workspace_size.argtypes = [i64, i64, i32]
     lib.moe_finalize_workspace_size.restype = sz
     for f in ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_run"):
@@ -185,3 +188,16 @@ def moe_quantize_run(x: torch.Tensor, quant_type: int, quant_scale: torch.Tensor
     _check(LIB.moe_quantize_run(_ptr(x), T, H, _ACT[x.dtype], int(quant_type), _ptr(quant_scale),
                                 _ptr(quant_out), _ptr(scale_out), int(sf_layout),
                                 _stream(x, stream)))
+
+
+def moe_residual_rmsnorm_run(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor,
+                             eps: float, residual_out: Optional[torch.Tensor],
+                             norm_out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> None:
+    if x.dtype not in _ACT:
+        raise ValueError(f"activation dtype {x.dtype} is not bf16/fp16")
+    T, H = x.shape
+    wp, wb = _ws(workspace)
+    _check(LIB.moe_residual_rmsnorm_run(_ptr(x), _ptr(residual), _ptr(gamma), float(eps),
+                                        _ptr(residual_out), _ptr(norm_out), wp, wb, T, H,
+                                        _ACT[x.dtype], _stream(x, stream)))

@@ -63,6 +63,7 @@ struct Params {
   int slot_span;             // slots covered by one workgroup (L * P)
   int slices;                // workgroups per token (> 1: the row is split, see below)
   uint8_t* ws;               // workspace of the split row modes (null when slices == 1)
+  int identity_routes;       // 1: no route map, token t's single route is row t (K = 1)
 };
 
 // Split rows. When a token's row is spread over `slices` workgroups, each workgroup publishes
@@ -206,7 +207,8 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   const int lane64 = tid & 63;
   const bool bf16_scales = a.scales_bf16 != 0;
   const uint32_t my_idx = __builtin_amdgcn_raw_buffer_load_b32(
-      rsrc(a.idx + (int64_t)t * a.K, (uint32_t)a.K * 4u), (uint32_t)lane64 * 4u, 0, 0);
+      rsrc(a.idx + (int64_t)t * a.K, a.identity_routes ? 0u : (uint32_t)a.K * 4u),
+      (uint32_t)lane64 * 4u, 0, 0);
   // Raw scale bits of both formats; the unused (or missing) one has an empty buffer. Loads are
   // predicated by buffer size, never by branches: a branch join makes the compiler wait for
   // every outstanding load before the row loads are issued.
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     for (int jj = 0; jj < CH; ++jj) {
       const int k = g + (c0 + jj) * G;
       const int kk = k < a.K ? k : 0;
-      const int pidx = __builtin_amdgcn_readlane((int)my_idx, kk);
+      const int pidx = a.identity_routes ? t : __builtin_amdgcn_readlane((int)my_idx, kk);
       present[jj] = k < a.K && (uint32_t)pidx < (uint32_t)a.n_rows;
       const uint32_t wbits = (uint32_t)__builtin_amdgcn_readlane((int)my_wbits, kk);
       // an absent route's scale is never used: its weight is 0 (and its row reads zeros)
@@ -671,7 +673,7 @@ static int to_code(hipError_t e) { return e == hipSuccess ? MOE_FIN_OK : MOE_FIN
 static int inputs_overlap(const Common& c, Range out) {
   const size_t e = 2;
   if (c.rows && overlap(out, rng(c.rows, (size_t)c.n_rows * c.H * e))) return 1;
-  if (overlap(out, rng(c.idx, (size_t)c.T * c.K * 4))) return 1;
+  if (c.idx && overlap(out, rng(c.idx, (size_t)c.T * c.K * 4))) return 1;
   if (c.scales && overlap(out, rng(c.scales, (size_t)c.T * c.K *
                                                  (c.scales_dtype == MOE_DTYPE_FP32 ? 4 : 2))))
     return 1;
@@ -684,7 +686,7 @@ static size_t workspace_bytes_for(int64_t T) { return kWsHeader + (size_t)T * kW
 static int run_rows(int mode, const Common& c, const void* residual, const void* gamma,
                     float eps, void* residual_out, void* norm_out, const float* qscale,
                     void* quant_out, void* scale_out, int sf_layout, void* workspace,
-                    void* stream) {
+                    void* stream, bool identity_routes = false) {
   const int slices = workspace ? choose_slices(c.T, (int)(c.H / 8)) : 1;
   Config cfg;
   if (!make_config(mode, c.T, (int)c.H, c.K, slices, &cfg)) return MOE_FIN_ERR_HIDDEN;
@@ -704,6 +706,7 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
   p.slot_span = cfg.span;
   p.slices = cfg.grid_x;
   p.ws = (uint8_t*)workspace;
+  p.identity_routes = identity_routes ? 1 : 0;
   hipStream_t s = (hipStream_t)stream;
   switch (mode) {
     case MODE_RMS: return to_code(dispatch<MODE_RMS>(c.act, p, cfg, s));
@@ -864,6 +867,31 @@ int moe_finalize_rmsnorm_run(const void* permuted_rows, int64_t num_permuted_row
     return rc;
   return run_rows(MODE_RMS, c, residual, gamma, eps, residual_out, norm_out, nullptr, nullptr,
                   nullptr, 0, workspace, stream);
+}
+
+int moe_residual_rmsnorm_run(const void* x, const void* residual, const void* gamma, float eps,
+                             void* residual_out, void* norm_out, void* workspace,
+                             size_t workspace_bytes, int64_t num_tokens, int64_t hidden,
+                             int act_dtype, void* stream) {
+  // The residual + RMSNorm of the finalize path on a given x: the finalize with one route per
+  // token (row t of x, weight 1), RSF 1 and no shared term reproduces x exactly.
+  Common c{x, num_tokens, nullptr, nullptr, MOE_DTYPE_FP32, nullptr, 1.0f, num_tokens, hidden,
+           1, act_dtype};
+  int rc = check_common(c, 8);
+  if (rc) return rc;
+  if (hidden > 16384) return MOE_FIN_ERR_HIDDEN;
+  if (num_tokens == 0) return MOE_FIN_OK;
+  if (!x) return MOE_FIN_ERR_NULL_POINTER;
+  if (!aligned(x, 16)) return MOE_FIN_ERR_ALIGNMENT;
+  if ((rc = check_rows(c, residual, gamma, residual_out, norm_out, true))) return rc;
+  const size_t tb = (size_t)num_tokens * hidden * 2;
+  if ((rc = check_workspace(c, workspace, workspace_bytes,
+                            {rng(residual, tb), rng(gamma, (size_t)hidden * 2),
+                             residual_out ? rng(residual_out, tb) : Range{0, 0},
+                             rng(norm_out, tb)})))
+    return rc;
+  return run_rows(MODE_RMS, c, residual, gamma, eps, residual_out, norm_out, nullptr, nullptr,
+                  nullptr, 0, workspace, stream, /*identity_routes=*/true);
 }
 
 int moe_quantize_run(const void* x, int64_t num_tokens, int64_t hidden, int act_dtype,

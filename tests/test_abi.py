@@ -153,3 +153,24 @@ def test_quantize_validation_codes():
     assert q(X, 4, 1024, 0, 1, QS, QO, None, 1, None) == -1
     assert q(X + 8, 4, 1024, 0, 1, QS, QO, SO, 1, None) == -5
     assert q(X, 4, 1024, 0, 1, QS, X + 1024, SO, 1, None) == -9
+
+
+def test_residual_rmsnorm_validation_codes():
+    f = LIB.moe_residual_rmsnorm_run
+    X, R, G, RO, NO = A, E, E + 0x100000, E + 0x200000, D
+
+    def call(x=X, res=R, g=G, ro=RO, no=NO, ws=None, wb=0, T=4, H=1024, act=0):
+        return f(x, res, g, 1e-6, ro, no, ws, wb, T, H, act, None)
+
+    assert call(act=3) == -6
+    assert call(H=1020) == -4 and call(H=16392) == -4 and call(H=0) == -4
+    assert call(T=-1) == -2
+    assert call(T=0) == 0 and call(T=0, x=None, res=None, g=None, no=None) == 0
+    assert call(x=None) == -1 and call(res=None) == -1 and call(g=None) == -1
+    assert call(no=None) == -1
+    assert call(x=X + 8) == -5 and call(ro=RO + 8) == -5
+    assert call(no=X) == -9 and call(ro=X + 4096) == -9      # outputs may not overlap x
+    need = M.moe_finalize_workspace_size(4, 1024, 1)
+    assert call(ws=WS + 64, wb=need) == -5
+    assert call(ws=WS, wb=need - 1) == -11
+    assert call(ws=X, wb=need) == -9

@@ -20,6 +20,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU containers
 import moe_expert_output_amd as M  # noqa: E402
 import oracle as O  # noqa: E402
 from synth import make_inputs, workload_seed  # noqa: E402
+from tests.comparators import ulp_distance  # noqa: E402
 from tests.parity import (bits16, check_finalize, check_norm, check_residual,  # noqa: E402
                           np64, oracle_ref, to_dev)
 
@@ -491,3 +492,81 @@ def test_quantize_rounding_midpoints_bit_exact():
 def test_large_batch(THK):
     T, H, K = THK
     full_check(make_inputs(T, H, K, seed=5000 + T + K))
+
+
+# ---- residual + RMSNorm of a given activation (moe_residual_rmsnorm_run) -------------------------
+def run_residual_rmsnorm(x, residual, gamma, eps, use_ws=True, inplace=False):
+    T, H = x.shape
+    no = torch.empty_like(x)
+    ro = residual if inplace else torch.empty_like(x)
+    ws = workspace(T) if use_ws else None
+    M.moe_residual_rmsnorm_run(x, residual, gamma, eps, ro, no, ws)
+    torch.cuda.synchronize()
+    assert ws_flag() == 0, "a split row timed out waiting for its slices"
+    return ro, no
+
+
+def _norm_within_1ulp(got_N, want_N, act):
+    fmt = O.FORMATS[act]
+    ud = ulp_distance(O.encode_bits(got_N, fmt), O.encode_bits(want_N, fmt))
+    assert ud.max() <= 1, (int(ud.max()), np.argwhere(ud > 1)[0])
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+@pytest.mark.parametrize("TH", [(1, 6144), (4, 1024), (37, 1032), (128, 7168), (300, 3584),
+                                (2, 16384), (5, 8)])
+def test_residual_rmsnorm(TH, act):
+    """r = RNE(x + residual) exactly (one float32 add of two activation values, rounded once,
+    equals the single rounding of the exact sum); norm within 1 ulp of the oracle's."""
+    T, H = TH
+    inp = make_inputs(T, H, 1, act_dtype=act, seed=5000 + T + (100 if act == "fp16" else 0))
+    _say(f"case residual_rmsnorm T={T} H={H} act={act} seed={inp.seed}")
+    x, res, gam = (inp.shared.cuda(), inp.residual.cuda(), inp.gamma.cuda())
+    R, N = O.residual_rmsnorm(np64(inp.shared), np64(inp.residual), np64(inp.gamma), inp.eps, act)
+    outs = []
+    for use_ws in (True, False):
+        ro, no = run_residual_rmsnorm(x, res, gam, inp.eps, use_ws=use_ws)
+        assert np.array_equal(np64(ro), R)
+        _norm_within_1ulp(np64(no), N, act)
+        outs.append((bits16(ro), bits16(no)))
+    # deterministic, and the in-place residual update gives the same results
+    ro2, no2 = run_residual_rmsnorm(x, res, gam, inp.eps)
+    assert np.array_equal(bits16(ro2), outs[0][0]) and np.array_equal(bits16(no2), outs[0][1])
+    res_io = res.clone()
+    ro3, no3 = run_residual_rmsnorm(x, res_io, gam, inp.eps, inplace=True)
+    assert ro3.data_ptr() == res_io.data_ptr()
+    assert np.array_equal(bits16(res_io), outs[0][0]) and np.array_equal(bits16(no3), outs[0][1])
+
+
+@pytest.mark.parametrize("THK", [(4, 1024, 8), (128, 7168, 8), (16, 2048, 22)])
+def test_two_kernel_path_matches_oracle(THK):
+    """moe_finalize_run followed by moe_residual_rmsnorm_run meets the same bars as the fused
+    moe_finalize_rmsnorm_run against the oracle."""
+    T, H, K = THK
+    inp = make_inputs(T, H, K, seed=workload_seed("larger", T) + 7 * K)
+    _say(f"case two-kernel T={T} H={H} K={K} seed={inp.seed}")
+    ref = oracle_ref(inp)
+    d = to_dev(inp)
+    s = run_finalize(inp, d)
+    check_finalize(np64(s), ref, "bf16")
+    ro, no = run_residual_rmsnorm(s, d["residual"], d["gamma"], inp.eps)
+    R, N = np64(ro), np64(no)
+    check_residual(R, ref, np64(inp.residual), "bf16")
+    check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")
+    # on this finalize's own rounded output the second kernel is exact in residual_out
+    R2, N2 = O.residual_rmsnorm(np64(s), np64(inp.residual), np64(inp.gamma), inp.eps, "bf16")
+    assert np.array_equal(R, R2)
+    _norm_within_1ulp(N, N2, "bf16")
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+def test_two_kernel_path_equals_fused_when_exact(act):
+    """Dyadic inputs (every float32 operation exact): the fused kernel and the two-kernel path
+    write the same residual_out bit for bit, and norms within 1 ulp of each other."""
+    inp = _dyadic_inputs(16, 2048 if act == "bf16" else 1024, 22, act, seed=95)
+    d = to_dev(inp)
+    ro_f, no_f = run_rmsnorm(inp, d)
+    s = run_finalize(inp, d)
+    ro_2, no_2 = run_residual_rmsnorm(s, d["residual"], d["gamma"], inp.eps)
+    assert np.array_equal(bits16(ro_f), bits16(ro_2))
+    _norm_within_1ulp(np64(no_2), np64(no_f), act)
