@@ -8,11 +8,15 @@ than twice the 256 MiB Infinity Cache, so rows come from HBM (cold). The calls a
 HIP graph and replayed; HIP events on the launch stream bracket exactly K calls.
 
 Output: one JSON line (metric, value = achieved algorithmic GB/s, us/call, roofline of the
-finalize kernel, the FP64 CPU oracle's throughput on the host as a baseline).
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu-baseline]
---sweep adds warm µs/call and the launch floor for every decode shape of the pages' workloads,
-and, for the hidden 1024/6144/7168 shapes, the unfused alternative (moe_finalize_run, then
-moe_residual_rmsnorm_run) beside the fused call.
+finalize kernel, the FP64 CPU oracle's throughput on the host as a baseline). Beside the HBM
+peak it reports the streaming ceiling: the library's plain stream kernel moving exactly the same
+bytes in one launch (every load issued up front, nothing else to do).
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep [--no-large]] [--no-cpu-baseline]
+--sweep adds, for every workload of the pages' configurations (decode shapes at hidden 1024, 6144
+and 7168, top-22/16/6/10 with fp32 and bf16 scales, NVFP4 / FP8 outputs) and the large-batch
+regime (T = 256..2048), warm µs/call against the launch floor, and from T = 32 on cold µs/call
+against the streaming ceiling of the same bytes; for the hidden 1024/6144/7168 shapes also the
+unfused alternative (moe_finalize_run, then moe_residual_rmsnorm_run) beside the fused call.
 """
 from __future__ import annotations
 
@@ -58,20 +62,31 @@ PEAK_GBS = 8000.0
 ACT_BYTES = 2
 
 
-def algorithmic_bytes(T, H, K, n_valid, scale_bytes=4, shared=True, entry="rmsnorm",
-                      quant=None):
-    """Bytes the path must move: valid rows, route metadata, shared, residual, gamma reads;
-    residual_out + norm_out writes (finalize-only: one output; quant: residual_out + codes + SF)."""
+def _read_bytes(T, H, K, n_valid, scale_bytes=4, shared=True, entry="rmsnorm"):
+    """Bytes the path must read: valid rows, route metadata, shared; + residual and gamma for the
+    RMSNorm entry points."""
     e = ACT_BYTES
     rd = n_valid * H * e + T * K * (4 + scale_bytes) + (T * H * e if shared else 0)
+    if entry != "finalize":
+        rd += T * H * e + H * e
+    return rd
+
+
+def algorithmic_bytes(T, H, K, n_valid, scale_bytes=4, shared=True, entry="rmsnorm",
+                      quant=None, norm_out=True):
+    """Bytes the path must move: valid rows, route metadata, shared, residual, gamma reads;
+    residual_out + norm_out writes (finalize-only: one output; quant: residual_out + codes + block
+    scales, + norm_out when it is stored)."""
+    e = ACT_BYTES
+    rd = _read_bytes(T, H, K, n_valid, scale_bytes, shared, entry)
     if entry == "finalize":
         return rd + T * H * e
-    rd += T * H * e + H * e
-    if quant == "nvfp4":
-        sf = ((T + 127) // 128 * 128) * ((H // 16 + 3) // 4 * 4)
-        return rd + T * H * e + T * H // 2 + sf
+    if quant in ("nvfp4", "nvfp4_linear"):
+        nb = H // 16
+        sf = ((T + 127) // 128 * 128) * ((nb + 3) // 4 * 4) if quant == "nvfp4" else T * nb
+        return rd + T * H * e + T * H // 2 + sf + (T * H * e if norm_out else 0)
     if quant == "fp8":
-        return rd + T * H * e + T * H
+        return rd + T * H * e + T * H + (T * H * e if norm_out else 0)
     return rd + 2 * T * H * e
 
 
@@ -82,6 +97,8 @@ def _parse():
     p.add_argument("--warmup", type=int, default=320)
     p.add_argument("--sets", type=int, default=32, help="input copies rotated per graph")
     p.add_argument("--sweep", action="store_true")
+    p.add_argument("--no-large", action="store_true", help="sweep without the T >= 256 cases")
+    p.add_argument("--groups", default="", help="comma-separated sweep groups to run (default all)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
@@ -164,6 +181,11 @@ def main():
     copy_us = _copy_reference(torch, stream, dev, nbytes, n_sets)
     floor = _warm_us(torch, stream, lambda: M.moe_finalize_launch_floor_run(1, T, H, K,
                                                                            device=dev))
+    # The streaming ceiling: the library's plain stream kernel moving the same bytes in one
+    # launch, rotated over the same amount of memory.
+    rd = _read_bytes(T, H, K, n_valid)
+    ceil_us = _stream_ceiling(torch, M, stream, dev, rd, nbytes - rd,
+                              min_rotate=n_sets * set_bytes)
     out = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -189,13 +211,17 @@ def main():
         "algorithmic_bytes_per_call": nbytes,
         "host_wall_s": round(t_host1 - t_host0, 4),
         "plain_copy_same_bytes_us": round(copy_us, 3),
+        "stream_ceiling_same_bytes_us": round(ceil_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "mfin::finalize_kernel<0, 1, 1, 1, 8> (bf16, RMSNorm, whole rows)",
-                     "per_launch_bytes": nbytes, "kernel_source_hash": kernel_source_hash()},
+                     "per_launch_bytes": nbytes, "kernel_source_hash": kernel_source_hash(),
+                     "stream_ceiling_GBs": round(nbytes / (ceil_us * 1e-6) / 1e9, 1),
+                     "frac_of_stream_ceiling": round(ceil_us / us_per_call, 4)},
     }
     if a.sweep:
-        out["cases"] = _sweep(torch, M, stream, dev, ws)
+        out["cases"] = _sweep(torch, M, stream, dev, large=not a.no_large,
+                              groups=[g for g in a.groups.split(",") if g])
     out["workspace_flag"] = int(ws[:4].view(torch.int32).item())
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, nbytes, a.cpu_seconds)
@@ -207,14 +233,34 @@ def _copy_reference(torch, stream, dev, nbytes, n_sets, replays=20):
     srcs = [torch.empty(half // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
             for _ in range(n_sets)]
     dsts = [torch.empty_like(x) for x in srcs]
+    return _graph_us(torch, stream, [(lambda s_=s_, d_=d_: d_.copy_(s_))
+                                     for s_, d_ in zip(srcs, dsts)], replays)
+
+
+def _stream_ceiling(torch, M, stream, dev, read_bytes, write_bytes, min_rotate=600 << 20,
+                    replays=20):
+    """µs per launch of the library's streaming-ceiling kernel moving the same bytes (cold:
+    source and destination rotate over more than twice the Infinity Cache)."""
+    rb, wb = read_bytes // 16 * 16, (write_bytes + 15) // 16 * 16
+    n = max(2, min(128, -(-min_rotate // max(rb + wb, 1))))
+    srcs = [torch.ones(max(rb, 16), dtype=torch.uint8, device=dev) for _ in range(n)]
+    dsts = [torch.empty(max(wb, 16), dtype=torch.uint8, device=dev) for _ in range(n)]
+    us = _graph_us(torch, stream, [(lambda s_=s_, d_=d_: M.moe_finalize_stream_floor_run(
+        s_, rb, d_, wb, stream=stream)) for s_, d_ in zip(srcs, dsts)], replays)
+    del srcs, dsts
+    return us
+
+
+def _graph_us(torch, stream, fns, replays):
+    """One HIP graph that makes each call of `fns` once, replayed; median µs per call."""
     with torch.cuda.stream(stream):
-        for s_, d_ in zip(srcs, dsts):
-            d_.copy_(s_)
+        for f in fns:
+            f()
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
-            for s_, d_ in zip(srcs, dsts):
-                d_.copy_(s_)
+            for f in fns:
+                f()
         times = []
         for _ in range(replays):
             e0 = torch.cuda.Event(enable_timing=True)
@@ -223,89 +269,168 @@ def _copy_reference(torch, stream, dev, nbytes, n_sets, replays=20):
             g.replay()
             e1.record(stream)
             e1.synchronize()
-            times.append(e0.elapsed_time(e1) * 1e3 / n_sets)
+            times.append(e0.elapsed_time(e1) * 1e3 / len(fns))
     return statistics.median(times)
 
 
 def _warm_us(torch, stream, fn, launches=20, replays=50):
-    with torch.cuda.stream(stream):
-        fn()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            for _ in range(launches):
-                fn()
-        times = []
-        for _ in range(replays):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1) * 1e3 / launches)
-    return statistics.median(times)
+    """The pages' protocol: one graph of `launches` calls on the same inputs, median of
+    `replays` replays, µs per call."""
+    return _graph_us(torch, stream, [fn] * launches, replays)
 
 
-def _sweep(torch, M, stream, dev, ws_big):
-    """µs/call for the pages' decode shapes: warm (same inputs) and cold (rotated copies)."""
+# Sweep cases: (group, entry, T, H, K, act, scales, shared, quant). entry: "rmsnorm" (fused
+# finalize + residual + RMSNorm), "finalize" (finalize only), "two_kernel" (finalize, then
+# moe_residual_rmsnorm_run), "quant" (moe_finalize_quant_run; quant = nvfp4 / nvfp4_linear /
+# fp8, "+norm" when norm_out is also stored), "quant_two_kernel" (moe_finalize_rmsnorm_run, then
+# moe_quantize_run of norm_out).
+def _sweep_cases(large):
+    c = [("tiny", e, 4, 1024, 8, "bf16", "fp32", True, None) for e in ("rmsnorm", "two_kernel")]
+    c += [("decode", e, t, 6144, 8, "bf16", "fp32", True, None) for t in (1, 4, 16)
+          for e in ("rmsnorm", "two_kernel")]
+    c += [("larger", e, t, 7168, 8, act, "fp32", True, None) for act in ("bf16", "fp16")
+          for t in (32, 64, 128) for e in ("rmsnorm", "two_kernel")]
+    c += [("highk", e, t, h, k, "bf16", sdt, False, None)
+          for (h, k) in ((2048, 22), (3584, 16), (2048, 6), (2048, 10))
+          for sdt in ("fp32", "bf16") for t in (1, 8, 16, 32) for e in ("finalize", "rmsnorm")]
+    c += [("quant", "quant", 64, 6144, 8, "bf16", "fp32", True, q)
+          for q in ("nvfp4", "nvfp4+norm", "nvfp4_linear", "fp8", "fp8+norm")]
+    c += [("quant", "quant_two_kernel", 64, 6144, 8, "bf16", "fp32", True, q)
+          for q in ("nvfp4+norm", "fp8+norm")]
+    c += [("quant", "rmsnorm", 64, 6144, 8, "bf16", "fp32", True, None)]
+    if large:
+        c += [("batch", e, t, 7168, 8, "bf16", "fp32", True, None) for t in (256, 512, 1024, 2048)
+              for e in ("rmsnorm", "finalize")]
+    return c
+
+
+def _sweep(torch, M, stream, dev, large=True, groups=()):
+    """Every case: warm µs/call (the pages' protocol) and the launch floor; from T = 32 on also
+    cold µs/call (inputs rotated over > 2x the Infinity Cache) and the streaming ceiling for the
+    same bytes. GB/s use the fused path's algorithmic bytes (the two-kernel path's extra write and
+    re-read of the finalize output is the cost the fusion removes)."""
     from synth import make_inputs, workload_seed
     cases = []
-    shapes = [("tiny", 4, 1024, 8, "bf16", "fp32", True)]
-    shapes += [("decode", t, 6144, 8, "bf16", "fp32", True) for t in (1, 4, 16)]
-    shapes += [("larger", t, 7168, 8, act, "fp32", True) for act in ("bf16", "fp16")
-               for t in (32, 64, 128)]
-    shapes += [("highk", t, h, k, "bf16", sdt, False) for (h, k) in ((2048, 22), (3584, 16))
-               for sdt in ("fp32",) for t in (1, 8, 16, 32)]
-    for (grp, T, H, K, act, sdt, sh) in shapes:
+    todo = [c for c in _sweep_cases(large) if not groups or c[0] in groups]
+    # one zero-filled workspace for every case (calls are serialized on one stream)
+    ws_big = torch.zeros(M.moe_finalize_workspace_size(max(c[2] for c in todo), 0, 0),
+                         dtype=torch.uint8, device=dev)
+    for (grp, entry, T, H, K, act, sdt, sh, quant) in todo:
+        print(f"sweep {grp} {entry} T={T} H={H} K={K} {act} {sdt} {quant or ''}", file=sys.stderr,
+              flush=True)
+        kvar = K if grp == "highk" else None
         inp = make_inputs(T, H, K, act_dtype=act, scale_dtype=sdt, with_shared=sh,
-                          seed=workload_seed(grp, T, act, sdt, K if grp == "highk" else None))
+                          seed=workload_seed(grp, T, act, sdt, kvar))
         n_valid = int((inp.idx >= 0).sum())
         dt = inp.rows.dtype
-        d = {k: (None if getattr(inp, k) is None else getattr(inp, k).to(dev)) for k in
-             ("rows", "idx", "scales", "shared", "residual", "gamma")}
-        ro = torch.empty(T, H, dtype=dt, device=dev)
-        no = torch.empty(T, H, dtype=dt, device=dev)
-        ws = ws_big
-        s_buf = torch.empty(T, H, dtype=dt, device=dev)
-        for entry in ("rmsnorm", "finalize", "two_kernel"):
-            if entry == "finalize" and grp not in ("highk",):
-                continue
-            if entry == "two_kernel" and grp not in ("tiny", "decode", "larger"):
-                continue
-            if entry == "two_kernel":
-                # the unfused alternative: finalize, then residual + RMSNorm as its own kernel
-                def fn(d=d, ro=ro, no=no, inp=inp, ws=ws, s_buf=s_buf):
-                    M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
-                                       s_buf)
-                    M.moe_residual_rmsnorm_run(s_buf, d["residual"], d["gamma"], inp.eps, ro, no,
-                                               ws)
+        qkind = (quant or "").split("+")[0]
+        keep_norm = quant is None or quant.endswith("+norm")
+        q_scale = None
+        if entry.startswith("quant"):
+            # the caller's per-tensor scale from the tensor's amax (448*6/amax or 448/amax)
+            probe = _dev_set(torch, inp, dev)
+            M.moe_finalize_rmsnorm_run(probe["rows"], probe["idx"], probe["scales"],
+                                       probe["shared"], inp.rsf, probe["residual"],
+                                       probe["gamma"], inp.eps, probe["ro"], probe["no"], ws_big)
+            amax = float(probe["no"].float().abs().max())
+            q_scale = torch.tensor([(2688.0 if qkind.startswith("nvfp4") else 448.0) / amax],
+                                   dtype=torch.float32, device=dev)
+            del probe
+        set_bytes = _set_bytes(inp, qkind)
+        cold = T >= 32
+        n_sets = max(2, min(128, -(-(600 << 20) // set_bytes))) if cold else 1
+        sets = [_dev_set(torch, inp, dev, qkind) for _ in range(n_sets)]
 
-                def floor_fn(T=T, H=H, K=K):               # two empty launches
-                    M.moe_finalize_launch_floor_run(0, T, H, K, device=dev)
-                    M.moe_finalize_launch_floor_run(1, T, H, 1, device=dev)
-            elif entry == "rmsnorm":
-                fn = (lambda d=d, ro=ro, no=no, inp=inp, ws=ws: M.moe_finalize_rmsnorm_run(
+        def fn_for(d, inp=inp, entry=entry, qkind=qkind, keep_norm=keep_norm, q_scale=q_scale):
+            if entry == "rmsnorm":
+                return lambda: M.moe_finalize_rmsnorm_run(
                     d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf, d["residual"],
-                    d["gamma"], inp.eps, ro, no, ws))
-                floor_fn = (lambda T=T, H=H, K=K:
-                            M.moe_finalize_launch_floor_run(1, T, H, K, device=dev))
-            else:
-                fn = (lambda d=d, no=no, inp=inp: M.moe_finalize_run(
-                    d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf, no))
-                floor_fn = (lambda T=T, H=H, K=K:
-                            M.moe_finalize_launch_floor_run(0, T, H, K, device=dev))
-            us = _warm_us(torch, stream, fn)
-            floor = _warm_us(torch, stream, floor_fn)
-            # the fused path's algorithmic bytes for both rmsnorm entries: the two-kernel
-            # path's extra write and re-read of s is the cost the fusion removes
-            nb = algorithmic_bytes(T, H, K, n_valid, 4 if sdt == "fp32" else 2, sh,
-                                   "rmsnorm" if entry == "two_kernel" else entry)
-            cases.append({"group": grp, "entry": entry, "T": T, "H": H, "K": K, "act": act,
-                          "scales": sdt, "us_warm": round(us, 3), "floor_us": round(floor, 3),
-                          "excess_us": round(us - floor, 3), "bytes": nb,
-                          "gbs_warm": round(nb / (us * 1e-6) / 1e9, 1)})
+                    d["gamma"], inp.eps, d["ro"], d["no"], ws_big, stream=stream)
+            if entry == "finalize":
+                return lambda: M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"],
+                                                  inp.rsf, d["no"], stream=stream)
+            if entry == "two_kernel":
+                def f():
+                    M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                       d["s"], stream=stream)
+                    M.moe_residual_rmsnorm_run(d["s"], d["residual"], d["gamma"], inp.eps,
+                                               d["ro"], d["no"], ws_big, stream=stream)
+                return f
+            qt = M.MOE_QUANT_FP8_E4M3 if qkind == "fp8" else M.MOE_QUANT_NVFP4
+            lay = M.MOE_SF_LINEAR if qkind == "nvfp4_linear" else M.MOE_SF_SWIZZLED_128x4
+            if entry == "quant_two_kernel":
+                # the unfused alternative: finalize + residual + RMSNorm, then quantize norm_out
+                def f2():
+                    M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"],
+                                               inp.rsf, d["residual"], d["gamma"], inp.eps,
+                                               d["ro"], d["no"], ws_big, stream=stream)
+                    M.moe_quantize_run(d["no"], qt, q_scale, d["q"], d.get("sf"), lay,
+                                       stream=stream)
+                return f2
+            return lambda: M.moe_finalize_quant_run(
+                d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf, d["residual"],
+                d["gamma"], inp.eps, qt, q_scale, d["q"], d.get("sf"), lay, d["ro"],
+                d["no"] if keep_norm else None, ws_big, stream=stream)
+
+        floor_entry = {"finalize": 0, "rmsnorm": 1, "quant": 2}.get(entry, 1)
+        if entry in ("two_kernel", "quant_two_kernel"):
+            def floor_fn(T=T, H=H, K=K):                 # two empty launches
+                M.moe_finalize_launch_floor_run(0, T, H, K, device=dev, stream=stream)
+                M.moe_finalize_launch_floor_run(1, T, H, 1, device=dev, stream=stream)
+        else:
+            def floor_fn(T=T, H=H, K=K, e=floor_entry):
+                M.moe_finalize_launch_floor_run(e, T, H, K, device=dev, stream=stream)
+        warm = _warm_us(torch, stream, fn_for(sets[0]))
+        floor = _warm_us(torch, stream, floor_fn)
+        base_entry = {"two_kernel": "rmsnorm", "quant_two_kernel": "quant"}.get(entry, entry)
+        nb = algorithmic_bytes(T, H, K, n_valid, 4 if sdt == "fp32" else 2, sh, base_entry,
+                               quant=qkind or None, norm_out=keep_norm)
+        rec = {"group": grp, "entry": entry, "T": T, "H": H, "K": K, "act": act, "scales": sdt,
+               "quant": quant, "us_warm": round(warm, 3), "floor_us": round(floor, 3),
+               "excess_us": round(warm - floor, 3), "bytes": nb,
+               "gbs_warm": round(nb / (warm * 1e-6) / 1e9, 1)}
+        if cold:
+            us = _graph_us(torch, stream, [fn_for(d) for d in sets],
+                           max(5, min(40, 2000 // n_sets)))
+            rd = _read_bytes(T, H, K, n_valid, 4 if sdt == "fp32" else 2, sh, base_entry)
+            del sets
+            ceil_us = _stream_ceiling(torch, M, stream, dev, rd, nb - rd)
+            rec.update({"sets": n_sets, "us_cold": round(us, 3),
+                        "gbs_cold": round(nb / (us * 1e-6) / 1e9, 1),
+                        "frac_peak_cold": round(nb / (us * 1e-6) / 1e9 / PEAK_GBS, 4),
+                        "stream_ceiling_us": round(ceil_us, 3),
+                        "frac_of_stream_ceiling": round(ceil_us / us, 3)})
+        else:
+            del sets
+        torch.cuda.empty_cache()
+        rec["workspace_flag"] = int(ws_big[:4].view(torch.int32).item())
+        cases.append(rec)
     return cases
+
+
+def _dev_set(torch, inp, dev, qkind=""):
+    T, H, dt = inp.T, inp.H, inp.rows.dtype
+    d = {k: (None if getattr(inp, k) is None else getattr(inp, k).to(dev).contiguous())
+         for k in ("rows", "idx", "scales", "shared", "residual", "gamma")}
+    d["ro"] = torch.empty(T, H, dtype=dt, device=dev)
+    d["no"] = torch.empty(T, H, dtype=dt, device=dev)
+    d["s"] = torch.empty(T, H, dtype=dt, device=dev)
+    if qkind:
+        import moe_expert_output_amd as M
+        fp8 = qkind == "fp8"
+        d["q"] = torch.empty(T, H if fp8 else H // 2, dtype=torch.uint8, device=dev)
+        if not fp8:
+            lay = M.MOE_SF_LINEAR if qkind == "nvfp4_linear" else M.MOE_SF_SWIZZLED_128x4
+            d["sf"] = torch.empty(M.moe_finalize_sf_size(T, H, lay), dtype=torch.uint8,
+                                  device=dev)
+    return d
+
+
+def _set_bytes(inp, qkind=""):
+    b = sum(getattr(inp, k).numel() * getattr(inp, k).element_size()
+            for k in ("rows", "idx", "scales", "shared", "residual", "gamma")
+            if getattr(inp, k) is not None)
+    return b + 3 * inp.T * inp.H * 2 + (inp.T * inp.H if qkind else 0)
 
 
 def _cpu_baseline(inp, nbytes, seconds):

@@ -232,6 +232,23 @@ size_t moe_finalize_sf_size(int64_t num_tokens, int64_t hidden, int sf_layout);
 int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden, int top_k,
                                   void* stream);
 
+/*
+ * moe_finalize_stream_floor_run -- measurement aid: read `read_bytes` from `src` and write
+ * `write_bytes` to `dst` in ONE kernel launch that does nothing else, the way an ideal finalize
+ * would move its bytes (every 128-bit load of a lane issued before any is used, nontemporal loads
+ * and stores). Its time per launch is the streaming ceiling for that many bytes in one launch on
+ * this device, which the finalize timings are compared against beside the HBM peak.
+ *   src  device memory, 16-byte aligned, read_bytes bytes (may be NULL if read_bytes == 0).
+ *   dst  device memory, 16-byte aligned, write_bytes bytes, overlapping no part of src. Content
+ *        written: with L = 256 * max(256, ceil(read_bytes / 16384)) lanes, 16-byte chunk j of dst
+ *        is the XOR of chunks (j % L) + i*L, i = 0..3, of src (chunks past the end read as 0).
+ * read_bytes and write_bytes must be multiples of 16 and at most 2^31. Errors:
+ * MOE_FIN_ERR_BAD_SHAPE, MOE_FIN_ERR_NULL_POINTER, MOE_FIN_ERR_ALIGNMENT, MOE_FIN_ERR_ALIAS,
+ * MOE_FIN_ERR_HIP. Both sizes 0 is a successful no-op.
+ */
+int moe_finalize_stream_floor_run(const void* src, size_t read_bytes, void* dst,
+                                  size_t write_bytes, void* stream);
+
 /* Static, NUL-terminated description of a return code. Host-only. */
 const char* moe_finalize_error_string(int code);
 

@@ -23,7 +23,7 @@ MOE_SF_LINEAR, MOE_SF_SWIZZLED_128x4 = 0, 1
 EXPORTED = ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_run",
             "moe_finalize_sf_size", "moe_finalize_error_string", "moe_finalize_version",
             "moe_finalize_launch_floor_run", "moe_finalize_workspace_size", "moe_quantize_run",
-            "moe_residual_rmsnorm_run")
+            "moe_residual_rmsnorm_run", "moe_finalize_stream_floor_run")
 
 _ACT = {torch.bfloat16: MOE_DTYPE_BF16, torch.float16: MOE_DTYPE_FP16}
 _SCALE = {torch.float32: MOE_DTYPE_FP32, torch.bfloat16: MOE_DTYPE_BF16}
@@ -63,6 +63,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_finalize_version.restype = ctypes.c_int
     lib.moe_finalize_launch_floor_run.argtypes = [i32, i64, i64, i32, vp]
     lib.moe_finalize_launch_floor_run.restype = ctypes.c_int
+    lib.moe_finalize_stream_floor_run.argtypes = [vp, sz, vp, sz, vp]
+    lib.moe_finalize_stream_floor_run.restype = ctypes.c_int
     return lib
 
 
@@ -98,6 +100,15 @@ def moe_finalize_launch_floor_run(entry: int, num_tokens: int, hidden: int, top_
         else torch.cuda.current_stream(dev).cuda_stream
     _check(LIB.moe_finalize_launch_floor_run(int(entry), int(num_tokens), int(hidden), int(top_k),
                                              s))
+
+
+def moe_finalize_stream_floor_run(src: torch.Tensor, read_bytes: int, dst: torch.Tensor,
+                                  write_bytes: int, stream=None) -> None:
+    for t, n in ((src, read_bytes), (dst, write_bytes)):
+        if n > t.numel() * t.element_size():
+            raise ValueError("byte count exceeds the tensor")
+    _check(LIB.moe_finalize_stream_floor_run(_ptr(src), int(read_bytes), _ptr(dst),
+                                             int(write_bytes), _stream(dst, stream)))
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

@@ -464,6 +464,33 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantParams a) {
 // launch-latency floor that the small-batch timings are reported against.
 __global__ __launch_bounds__(1024) void launch_floor_kernel(int) {}
 
+// Measurement aid: move n_rd 16-byte chunks in and n_wr chunks out in one launch, the way a
+// perfect finalize would (every load of a lane issued before any is used, nontemporal loads and
+// stores), with nothing else to do. Its time is the single-launch streaming ceiling for a given
+// number of bytes, which the finalize timings are compared against. Each lane reads up to
+// kStreamLoads chunks (lane + i * lanes), folds them with XOR, and stores the fold at every
+// output chunk j with j % lanes == lane; chunks past the end read zeros.
+constexpr int kStreamLoads = 4;
+__global__ __launch_bounds__(256) void stream_floor_kernel(const uint8_t* src, uint32_t n_rd,
+                                                           uint8_t* dst, uint32_t n_wr) {
+  const uint32_t lanes = gridDim.x * 256u;
+  const uint32_t lane = blockIdx.x * 256u + threadIdx.x;
+  const auto rd = rsrc(src, n_rd * 16u);
+  const auto wr = rsrc(dst, n_wr * 16u);
+  u32x4 v[kStreamLoads];
+#pragma unroll
+  for (int i = 0; i < kStreamLoads; ++i)
+    v[i] = __builtin_amdgcn_raw_buffer_load_b128(rd, (lane + (uint32_t)i * lanes) * 16u, 0, 2);
+  u32x4 fold = v[0];
+#pragma unroll
+  for (int i = 1; i < kStreamLoads; ++i) fold ^= v[i];
+  // every lane consumes its loads here, so none is moved into the store loop (which lanes past
+  // the last output chunk skip)
+  asm volatile("" ::"v"(fold));
+  for (uint32_t j = lane; j < n_wr; j += lanes)
+    __builtin_amdgcn_raw_buffer_store_b128(fold, wr, j * 16u, 0, 2);
+}
+
 // ------------------------------------------------------------------------------------------------
 // Host side: launch configuration and dispatch.
 // ------------------------------------------------------------------------------------------------
@@ -812,6 +839,26 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
   if ((int64_t)c.grid_x * num_tokens > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
   hipLaunchKernelGGL(launch_floor_kernel, dim3((unsigned)(c.grid_x * num_tokens)), dim3(c.G * c.L),
                      c.lds, (hipStream_t)stream, 0);
+  return to_code(hipGetLastError());
+}
+
+int moe_finalize_stream_floor_run(const void* src, size_t read_bytes, void* dst,
+                                  size_t write_bytes, void* stream) {
+  const size_t kMax = (size_t)1 << 31;
+  if (read_bytes % 16 != 0 || write_bytes % 16 != 0 || read_bytes > kMax || write_bytes > kMax)
+    return MOE_FIN_ERR_BAD_SHAPE;
+  if ((read_bytes && !src) || (write_bytes && !dst)) return MOE_FIN_ERR_NULL_POINTER;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_FIN_ERR_ALIGNMENT;
+  if (read_bytes && write_bytes && overlap(rng(src, read_bytes), rng(dst, write_bytes)))
+    return MOE_FIN_ERR_ALIAS;
+  const uint32_t n_rd = (uint32_t)(read_bytes / 16), n_wr = (uint32_t)(write_bytes / 16);
+  if (n_rd == 0 && n_wr == 0) return MOE_FIN_OK;
+  // one 256-lane workgroup per kStreamLoads * 256 chunks read, at least one per CU
+  const uint32_t per_wg = 256u * kStreamLoads;
+  uint32_t grid = (n_rd + per_wg - 1) / per_wg;
+  if (grid < 256u) grid = 256u;
+  hipLaunchKernelGGL(stream_floor_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                     (const uint8_t*)src, n_rd, (uint8_t*)dst, n_wr);
   return to_code(hipGetLastError());
 }
 

@@ -129,6 +129,17 @@ def test_launch_floor_validation_codes():
     assert f(1, 0, 1024, 8, None) == 0
 
 
+def test_stream_floor_validation_codes():
+    f = LIB.moe_finalize_stream_floor_run
+    S, Dst = A, E
+    assert f(S, 1000, Dst, 1024, None) == -2 and f(S, 1024, Dst, 24, None) == -2
+    assert f(S, (1 << 31) + 16, Dst, 0, None) == -2
+    assert f(None, 1024, Dst, 0, None) == -1 and f(S, 0, None, 1024, None) == -1
+    assert f(S + 8, 1024, Dst, 1024, None) == -5 and f(S, 1024, Dst + 4, 1024, None) == -5
+    assert f(S, 4096, S + 1024, 1024, None) == -9
+    assert f(None, 0, None, 0, None) == 0
+
+
 def test_quant_validation_codes():
     assert quant(qt=0) == -7 and quant(qt=3) == -7
     assert quant(layout=2) == -8               # SWIZZLED_8x4 is not accepted

@@ -487,6 +487,62 @@ def test_quantize_rounding_midpoints_bit_exact():
                           O.quant_fp8(N8, 1.0))
 
 
+def _act_vals(x, act):
+    return O.round_to_format(np.asarray(x, dtype=np.float64), O.BF16 if act == "bf16" else O.FP16)
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+def test_quantize_near_midpoints_bit_exact(act):
+    """Scales chosen so that x * scale lands within a float32 rounding of a rounding midpoint
+    without being equal to it (the float32 product rounds onto the midpoint, the exact product
+    is just above or below): FP8 codes, NVFP4 block scales and E2M1 codes must still follow the
+    exact product, as the oracle does."""
+    rng = np.random.default_rng(77 if act == "bf16" else 78)
+    e4 = O.decode_bits(np.arange(0x7F, dtype=np.uint8), O.E4M3)
+    m4 = (e4[:-1] + e4[1:]) / 2                       # E4M3 rounding midpoints
+    m2 = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    ks = np.arange(-6, 6)
+    for draw in range(16):
+        x0 = float(_act_vals(rng.uniform(1, 2), act))
+        # FP8: s8 = fl32(mid / x0); elements x0 * 2^k hit the midpoints mid * 2^k (normal range)
+        mid = float(m4[rng.integers(16, 100)])
+        s8 = float(np.float32(mid / x0))
+        vals = np.concatenate([x0 * 2.0 ** ks, -x0 * 2.0 ** ks, _act_vals(rng.normal(size=40), act)])
+        N = np.zeros((1, 64))
+        N[0, :len(vals)] = vals
+        got, _ = _quantize_dev(N, act, M.MOE_QUANT_FP8_E4M3, s8, 0)
+        assert np.array_equal(got, O.quant_fp8(N, s8)), ("fp8", draw, s8)
+        # NVFP4 E2M1 codes: gs = fl32(mid2 / x0) with block scale 1 (block amax a ~ 6 / gs), and
+        # the same at block scales 2^k
+        mid2 = float(m2[rng.integers(0, 7)])
+        gs = float(np.float32(mid2 / x0))
+        a = float(_act_vals(6.0 / gs, act))
+        rows = []
+        for k in range(-4, 4):
+            blk = np.zeros(16)
+            blk[0] = a * 2.0 ** k
+            blk[1:4] = np.array([x0, -x0, x0]) * 2.0 ** k
+            blk[4:] = _act_vals(rng.uniform(-1, 1, 12) * a * 2.0 ** k, act)
+            rows.append(blk)
+        # NVFP4 block scales: gs2 = fl32(6 * mid4 / a0), blocks with amax a0 * 2^k
+        a0 = x0
+        mid4 = float(m4[rng.integers(40, 100)])
+        gs2 = float(np.float32(6.0 * mid4 / a0))
+        N2 = np.concatenate(rows).reshape(2, 64)
+        want_c, want_s = O.quant_nvfp4(N2, gs, 1)
+        got_c, got_s = _quantize_dev(N2, act, M.MOE_QUANT_NVFP4, gs, 1)
+        assert np.array_equal(got_c, want_c) and np.array_equal(got_s, want_s), ("e2m1", draw)
+        rows = []
+        for k in range(-3, 5):
+            blk = _act_vals(rng.uniform(-1, 1, 16) * a0 * 2.0 ** k, act)
+            blk[rng.integers(0, 16)] = -a0 * 2.0 ** k if k % 2 else a0 * 2.0 ** k
+            rows.append(blk)
+        N3 = np.concatenate(rows).reshape(2, 64)
+        want_c, want_s = O.quant_nvfp4(N3, gs2, 1)
+        got_c, got_s = _quantize_dev(N3, act, M.MOE_QUANT_NVFP4, gs2, 1)
+        assert np.array_equal(got_c, want_c) and np.array_equal(got_s, want_s), ("scale", draw)
+
+
 # ---- large batches (prefill-sized calls: whole rows, nontemporal streaming) ---------------------
 @pytest.mark.parametrize("THK", [(256, 7168, 8), (512, 7168, 8), (2048, 2048, 8), (300, 3584, 16)])
 def test_large_batch(THK):
@@ -570,3 +626,28 @@ def test_two_kernel_path_equals_fused_when_exact(act):
     ro_2, no_2 = run_residual_rmsnorm(s, d["residual"], d["gamma"], inp.eps)
     assert np.array_equal(bits16(ro_f), bits16(ro_2))
     _norm_within_1ulp(np64(no_2), np64(no_f), act)
+
+
+@pytest.mark.parametrize("rb,wb", [(16 * 1000, 16 * 300), (14_680_064, 3_670_016),
+                                   (16 * 5 * 262144 + 48, 16 * 70000), (0, 4096), (4096, 0)])
+def test_stream_floor_writes_documented_fold(rb, wb):
+    """The streaming-ceiling kernel (a measurement aid) writes exactly its documented content and
+    nothing past write_bytes."""
+    _say(f"stream floor read {rb} write {wb}")
+    g = torch.Generator().manual_seed(rb + wb)
+    src = torch.randint(0, 2 ** 31, (max(rb, 16) // 4,), generator=g, dtype=torch.int32)
+    dst = torch.full(((wb + 4096) // 4,), -7, dtype=torch.int32)
+    sd, dd = src.cuda(), dst.cuda()
+    M.moe_finalize_stream_floor_run(sd, rb, dd, wb)
+    torch.cuda.synchronize()
+    got = dd.cpu().numpy()
+    chunks = src.numpy().view(np.uint32).reshape(-1, 4)[: rb // 16]
+    lanes = 256 * max(256, -(-rb // 16384))
+    fold = np.zeros((lanes, 4), dtype=np.uint32)
+    for i in range(4):
+        part = chunks[i * lanes:(i + 1) * lanes]
+        fold[: len(part)] ^= part
+    n_wr = wb // 16
+    want = fold[np.arange(n_wr) % lanes]
+    assert np.array_equal(got[: n_wr * 4].view(np.uint32).reshape(-1, 4), want)
+    assert np.all(got[n_wr * 4:] == -7)
