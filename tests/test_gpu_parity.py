@@ -651,3 +651,128 @@ def test_stream_floor_writes_documented_fold(rb, wb):
     want = fold[np.arange(n_wr) % lanes]
     assert np.array_equal(got[: n_wr * 4].view(np.uint32).reshape(-1, 4), want)
     assert np.all(got[n_wr * 4:] == -7)
+
+
+# ---- cancellation / high dynamic range (float32 accumulation, rounded once) -----------------------
+def _cancelling_inputs(T, H, act, seed):
+    """Per token: three pairs of large routed terms (+x, -x, equal weights) that cancel exactly,
+    one small route, one absent route, in a random route order (partners may land in different
+    route groups). Large terms are m * 2^5 (|m| <= 127, up to 2^12), small ones m * 2^-4 with
+    weight 1/2, shared m * 2^-3, RSF 2: every partial sum of any float32 order spans at most 21
+    significant bits, so the kernel's float32 value before its one rounding is exactly S*; per-step
+    rounding to the activation dtype loses the small terms next to the large ones."""
+    K = 8
+    rng = np.random.Generator(np.random.PCG64(seed))
+    n_rows = T * K
+    inp = make_inputs(T, H, K, seed=seed, act_dtype=act, n_rows=n_rows)
+    dt = ACT_T[act]
+    rows = np.zeros((n_rows, H), dtype=np.float32)
+    idx = np.full((T, K), -1, dtype=np.int32)
+    sc = np.zeros((T, K), dtype=np.float32)
+    nxt = 0
+    for t in range(T):
+        slots = rng.permutation(K)
+        for p in range(3):
+            big = rng.integers(-127, 128, H).astype(np.float32) * 32.0
+            w = float(np.ldexp(1.0, int(rng.integers(-1, 1))))
+            for sign, k in ((1.0, slots[2 * p]), (-1.0, slots[2 * p + 1])):
+                rows[nxt] = sign * big
+                idx[t, k] = nxt
+                sc[t, k] = w
+                nxt += 1
+        rows[nxt] = rng.integers(-127, 128, H).astype(np.float32) / 16.0
+        idx[t, slots[6]] = nxt
+        sc[t, slots[6]] = 0.5
+        nxt += 1
+        sc[t, slots[7]] = 0.25               # absent route: its weight must not matter
+    inp.rows = torch.from_numpy(rows).to(dt)
+    inp.idx = torch.from_numpy(idx)
+    inp.scales = torch.from_numpy(sc)
+    inp.shared = torch.from_numpy(rng.integers(-64, 65, (T, H)).astype(np.float32) / 8.0).to(dt)
+    inp.rsf = 2.0
+    return inp
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+@pytest.mark.parametrize("TH", [(5, 1032), (64, 7168)])
+def test_cancellation_high_dynamic_range_bit_exact(TH, act):
+    T, H = TH
+    inp = _cancelling_inputs(T, H, act, seed=600 + T)
+    ref = oracle_ref(inp)
+    fmt = O.FORMATS[act]
+    # the fixture separates the two numerics: per-step rounding misses the small terms
+    old = O.finalize_per_step_rounding(np64(inp.rows), inp.idx.numpy(), np64(inp.scales),
+                                       np64(inp.shared), inp.rsf, act)
+    assert np.mean(old != ref.s) > 0.3
+    s = run_finalize(inp)
+    assert np.array_equal(bits16(s), O.encode_bits(ref.s, fmt).astype(np.int64))
+    for use_ws in (True, False):
+        ro, no = run_rmsnorm(inp, use_ws=use_ws)
+        assert np.array_equal(bits16(ro), O.encode_bits(ref.R, fmt).astype(np.int64))
+        check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, act)
+
+
+# ---- every output stays inside its buffer; inputs are never written -----------------------------
+GUARD = 4096
+
+
+def _guarded(nbytes, dtype, shape):
+    """A view of `shape` inside a buffer with GUARD bytes of 0x5A before and after it."""
+    full = torch.full((GUARD + nbytes + GUARD,), 0x5A, dtype=torch.uint8, device="cuda")
+    return full, full[GUARD:GUARD + nbytes].view(dtype).view(shape)
+
+
+def _guards_intact(full):
+    g = full.cpu().numpy()
+    return bool((g[:GUARD] == 0x5A).all() and (g[-GUARD:] == 0x5A).all())
+
+
+@pytest.mark.parametrize("THK", [(5, 1032, 8), (37, 7168, 8), (130, 2048, 22), (3, 48, 6)])
+def test_outputs_stay_in_bounds_and_inputs_untouched(THK):
+    T, H, K = THK
+    _say(f"guards T={T} H={H} K={K}")
+    inp = make_inputs(T, H, K, seed=700 + T)
+    d = to_dev(inp)
+    before = {k: v.clone() for k, v in d.items() if v is not None}
+    tb = T * H * 2
+    ws_full, ws = _guarded(M.moe_finalize_workspace_size(T, H, K), torch.uint8, (-1,))
+    ws.zero_()
+    outs = []
+
+    def new(nbytes, dtype, shape):
+        full, view = _guarded(nbytes, dtype, shape)
+        outs.append(full)
+        return view
+
+    M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                       new(tb, torch.bfloat16, (T, H)))
+    for w in (ws, None):
+        M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                   d["residual"], d["gamma"], inp.eps,
+                                   new(tb, torch.bfloat16, (T, H)),
+                                   new(tb, torch.bfloat16, (T, H)), w)
+    qs = torch.tensor([3.0], dtype=torch.float32, device="cuda")
+    x = torch.randn(T, H, device="cuda").to(torch.bfloat16)
+    for layout in ((M.MOE_SF_SWIZZLED_128x4, M.MOE_SF_LINEAR) if H % 16 == 0 else ()):
+        sfb = M.moe_finalize_sf_size(T, H, layout)
+        M.moe_finalize_quant_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                 d["residual"], d["gamma"], inp.eps, M.MOE_QUANT_NVFP4, qs,
+                                 new(tb // 4, torch.uint8, (T, H // 2)),
+                                 new(sfb, torch.uint8, (-1,)), layout,
+                                 new(tb, torch.bfloat16, (T, H)), new(tb, torch.bfloat16, (T, H)),
+                                 ws)
+        M.moe_quantize_run(x, M.MOE_QUANT_NVFP4, qs, new(tb // 4, torch.uint8, (T, H // 2)),
+                           new(sfb, torch.uint8, (-1,)), layout)
+    M.moe_finalize_quant_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                             d["residual"], d["gamma"], inp.eps, M.MOE_QUANT_FP8_E4M3, qs,
+                             new(tb // 2, torch.uint8, (T, H)), None, 0,
+                             new(tb, torch.bfloat16, (T, H)), None, ws)
+    M.moe_quantize_run(x, M.MOE_QUANT_FP8_E4M3, qs, new(tb // 2, torch.uint8, (T, H)), None, 0)
+    M.moe_residual_rmsnorm_run(x, d["residual"], d["gamma"], inp.eps,
+                               new(tb, torch.bfloat16, (T, H)), new(tb, torch.bfloat16, (T, H)),
+                               ws)
+    torch.cuda.synchronize()
+    assert all(_guards_intact(f) for f in outs)
+    assert _guards_intact(ws_full) and int(ws[:4].view(torch.int32).item()) == 0
+    for k, v in before.items():
+        assert torch.equal(d[k], v), k
