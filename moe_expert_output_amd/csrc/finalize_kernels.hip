@@ -174,8 +174,9 @@ __device__ __forceinline__ void zero_sf_padding(const QuantDst& d, int T, int t,
   }
 }
 
-// NT = 2 marks the row loads and the residual_out stores nontemporal (streamed once; chosen for
-// large calls), NT = 0 leaves them cacheable.
+// NT = 2 marks the streamed accesses nontemporal (chosen for large calls): the row, shared and
+// residual loads and the residual_out and norm_out stores; gamma, shared by every token, stays
+// cacheable. NT = 0 leaves them all cacheable.
 template <int ACT, int MODE, int G, int P, int JMAX, int NT>
 __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   // blockIdx.x = token * slices + slice (one slice per token in the whole-row modes)
@@ -238,13 +239,13 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   {
     const auto sh_r = rsrc(a.shared + tok_off, (g == 0 && a.shared) ? row_bytes : 0u);
 #pragma unroll
-    for (int p = 0; p < P; ++p) shv[p] = __builtin_amdgcn_raw_buffer_load_b128(sh_r, voff[p], 0, 0);
+    for (int p = 0; p < P; ++p) shv[p] = __builtin_amdgcn_raw_buffer_load_b128(sh_r, voff[p], 0, NT);
     if constexpr (MODE != MODE_FIN) {
       const auto res_r = rsrc(a.residual + tok_off, g == 0 ? row_bytes : 0u);
       const auto gam_r = rsrc(a.gamma, g == 0 ? row_bytes : 0u);
 #pragma unroll
       for (int p = 0; p < P; ++p) {
-        resv[p] = __builtin_amdgcn_raw_buffer_load_b128(res_r, voff[p], 0, 0);
+        resv[p] = __builtin_amdgcn_raw_buffer_load_b128(res_r, voff[p], 0, NT);
         gamv[p] = __builtin_amdgcn_raw_buffer_load_b128(gam_r, voff[p], 0, 0);
       }
     }
@@ -415,7 +416,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) n[e] = (r[p][e] * rinv) * gm[e];
     const u32x4 n_pk = Act<ACT>::pack(n);
-    __builtin_amdgcn_raw_buffer_store_b128(n_pk, no_r, voff[p], 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(n_pk, no_r, voff[p], 0, NT);
     if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) {
       float nr[8];
       Act<ACT>::unpack(n_pk, nr);               // quantize the rounded norm_out values
@@ -500,9 +501,10 @@ struct Config {
   bool nontemporal;
 };
 
-// Rows are read exactly once. Above 4 MiB of rows per call, nontemporal row loads and
-// residual_out stores measured 10-14 % faster with the data in HBM (T = 64, 128 at hidden 7168);
-// below it they were slower, so small calls keep cacheable accesses.
+// Rows are read exactly once. Above 4 MiB of rows per call, nontemporal accesses to the streamed
+// tensors (row, shared and residual loads; residual_out and norm_out stores) measured 5-18 %
+// faster with the inputs in HBM (T = 64..256 at hidden 7168); below it they were no faster or
+// slower, so small calls keep cacheable accesses.
 constexpr int64_t kNontemporalRowBytes = (int64_t)4 << 20;
 static bool use_nontemporal(int64_t T, int64_t H, int K) {
   return T * (int64_t)K * H * 2 >= kNontemporalRowBytes;
