@@ -776,3 +776,35 @@ def test_outputs_stay_in_bounds_and_inputs_untouched(THK):
     assert _guards_intact(ws_full) and int(ws[:4].view(torch.int32).item()) == 0
     for k, v in before.items():
         assert torch.equal(d[k], v), k
+
+
+def test_split_row_timeout_is_flagged_and_bounded():
+    """Failure detection of the split-row exchange, forced from the host: one token's workspace
+    slots are set so that its two slices expect different epochs and can never agree. Each slice
+    gives up after the kernel's own bounded wait, sets the sticky flag in the workspace header and
+    exits; the call completes. A zero-filled workspace then works again."""
+    import time
+    inp = make_inputs(1, 1024, 8, seed=800)          # T=1, hidden 1024: two slices per row
+    d = to_dev(inp)
+    need = M.moe_finalize_workspace_size(1, 1024, 8)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    slots = ws[256:256 + 512].view(torch.int64)
+    slots[0::2] = 5 << 32                             # slice 0 will wait for epoch 6 ...
+    slots[1::2] = 9 << 32                             # ... slice 1 for epoch 10
+    ro = torch.empty(1, 1024, dtype=torch.bfloat16, device="cuda")
+    no = torch.empty_like(ro)
+    _say("forcing a split-row timeout (bounded wait, a few seconds)")
+    t0 = time.time()
+    M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                               d["residual"], d["gamma"], inp.eps, ro, no, ws)
+    torch.cuda.synchronize()
+    _say(f"  returned after {time.time() - t0:.2f} s")
+    assert int(ws[:4].view(torch.int32).item()) == 1
+    ws.zero_()
+    ref = oracle_ref(inp)
+    M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                               d["residual"], d["gamma"], inp.eps, ro, no, ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0
+    check_residual(np64(ro), ref, np64(inp.residual), "bf16")
+    check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, "bf16")
