@@ -69,8 +69,11 @@ MAX_SETS = 384
 
 def _read_bytes(T, H, K, n_valid, scale_bytes=4, shared=True, entry="rmsnorm"):
     """Bytes the path must read: valid rows, route metadata, shared; + residual and gamma for the
-    RMSNorm entry points."""
+    RMSNorm entry points. The rank sum reads K = world_size partial rows per token and no route
+    metadata."""
     e = ACT_BYTES
+    if entry == "rank_sum":
+        return K * T * H * e + T * H * e + H * e
     rd = n_valid * H * e + T * K * (4 + scale_bytes) + (T * H * e if shared else 0)
     if entry != "finalize":
         rd += T * H * e + H * e
@@ -289,7 +292,7 @@ def _warm_us(torch, stream, fn, launches=20, replays=50):
 # finalize + residual + RMSNorm), "finalize" (finalize only), "two_kernel" (finalize, then
 # moe_residual_rmsnorm_run), "quant" (moe_finalize_quant_run; quant = nvfp4 / nvfp4_linear /
 # fp8, "+norm" when norm_out is also stored), "quant_two_kernel" (moe_finalize_rmsnorm_run, then
-# moe_quantize_run of norm_out).
+# moe_quantize_run of norm_out), "rank_sum" (moe_rank_sum_rmsnorm_run of K = world_size partials).
 def _sweep_cases(large):
     c = [("tiny", e, 4, 1024, 8, "bf16", "fp32", True, None) for e in ("rmsnorm", "two_kernel")]
     c += [("decode", e, t, 6144, 8, "bf16", "fp32", True, None) for t in (1, 4, 16)
@@ -304,6 +307,9 @@ def _sweep_cases(large):
     c += [("quant", "quant_two_kernel", 64, 6144, 8, "bf16", "fp32", True, q)
           for q in ("nvfp4+norm", "fp8+norm")]
     c += [("quant", "rmsnorm", 64, 6144, 8, "bf16", "fp32", True, None)]
+    # one GPU's share of the cross-rank reduction at the pages' TP4 shapes (world size 4)
+    c += [("ranksum", "rank_sum", t, h, 4, "bf16", None, False, None)
+          for (h, ts) in ((6144, (1, 16)), (7168, (1, 16, 64, 128))) for t in ts]
     if large:
         c += [("batch", e, t, 7168, 8, "bf16", "fp32", True, None) for t in (256, 512, 1024, 2048)
               for e in ("rmsnorm", "finalize")]
@@ -326,7 +332,8 @@ def _sweep(torch, M, stream, dev, large=True, groups=()):
               flush=True)
         kvar = K if grp == "highk" else None
         inp = make_inputs(T, H, K, act_dtype=act, scale_dtype=sdt, with_shared=sh,
-                          seed=workload_seed(grp, T, act, sdt, kvar))
+                          seed=workload_seed(grp, T, act, sdt, kvar),
+                          mask_frac=0.0 if entry == "rank_sum" else 0.25)
         n_valid = int((inp.idx >= 0).sum())
         dt = inp.rows.dtype
         qkind = (quant or "").split("+")[0]
@@ -355,6 +362,11 @@ def _sweep(torch, M, stream, dev, large=True, groups=()):
             if entry == "finalize":
                 return lambda: M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"],
                                                   inp.rsf, d["no"], stream=stream)
+            if entry == "rank_sum":
+                parts = d["rows"].view(inp.K, inp.T, inp.H)
+                return lambda: M.moe_rank_sum_rmsnorm_run(parts, d["residual"], d["gamma"],
+                                                          inp.eps, d["ro"], d["no"], ws_big,
+                                                          stream=stream)
             if entry == "two_kernel":
                 def f():
                     M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
@@ -378,7 +390,7 @@ def _sweep(torch, M, stream, dev, large=True, groups=()):
                 d["gamma"], inp.eps, qt, q_scale, d["q"], d.get("sf"), lay, d["ro"],
                 d["no"] if keep_norm else None, ws_big, stream=stream)
 
-        floor_entry = {"finalize": 0, "rmsnorm": 1, "quant": 2}.get(entry, 1)
+        floor_entry = {"finalize": 0, "rmsnorm": 1, "quant": 2, "rank_sum": 1}.get(entry, 1)
         if entry in ("two_kernel", "quant_two_kernel"):
             def floor_fn(T=T, H=H, K=K):                 # two empty launches
                 M.moe_finalize_launch_floor_run(0, T, H, K, device=dev, stream=stream)
@@ -389,8 +401,11 @@ def _sweep(torch, M, stream, dev, large=True, groups=()):
         warm = _warm_us(torch, stream, fn_for(sets[0]))
         floor = _warm_us(torch, stream, floor_fn)
         base_entry = {"two_kernel": "rmsnorm", "quant_two_kernel": "quant"}.get(entry, entry)
-        nb = algorithmic_bytes(T, H, K, n_valid, 4 if sdt == "fp32" else 2, sh, base_entry,
-                               quant=qkind or None, norm_out=keep_norm)
+        if entry == "rank_sum":
+            nb = _read_bytes(T, H, K, n_valid, entry="rank_sum") + 2 * T * H * ACT_BYTES
+        else:
+            nb = algorithmic_bytes(T, H, K, n_valid, 4 if sdt == "fp32" else 2, sh, base_entry,
+                                   quant=qkind or None, norm_out=keep_norm)
         rec = {"group": grp, "entry": entry, "T": T, "H": H, "K": K, "act": act, "scales": sdt,
                "quant": quant, "us_warm": round(warm, 3), "floor_us": round(floor, 3),
                "excess_us": round(warm - floor, 3), "bytes": nb,

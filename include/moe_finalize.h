@@ -212,6 +212,39 @@ int moe_residual_rmsnorm_run(const void* x, const void* residual, const void* ga
                              int64_t num_tokens, int64_t hidden, int act_dtype, void* stream);
 
 /*
+ * moe_rank_sum_rmsnorm_run -- one GPU's share of the cross-rank reduction that the pages fuse
+ * between the finalize and the residual + RMSNorm ([FI6631] Description: the per-rank finalized
+ * partials are summed in float32 and rounded once before the residual add and RMSNorm;
+ * [FI3385] commit notes: every rank accumulates the ranks in the same fixed order). Given the
+ * world_size partial rows that the ranks' finalize calls produced for the same tokens (already
+ * gathered into this GPU's memory by the transport, which is not part of this library):
+ *   s    = RNE_T(sum over r of partial[r, t, h])        (float32 sum, one rounding)
+ *   r, norm as in moe_finalize_rmsnorm_run.
+ * It is moe_finalize_rmsnorm_run with one route per rank (row r*T + t, weight 1), routed scaling
+ * 1 and no shared term, so the sum follows the same fixed, timing-independent order on every
+ * rank and call, and every result lies in the same float32 window as the finalize's.
+ *
+ *   rank_partials  [world_size, num_tokens, hidden] act_dtype, 16-byte aligned: rank r's rows.
+ *   world_size     1..64 (MOE_FIN_ERR_BAD_TOPK otherwise); world_size * num_tokens <= 2^31 - 1.
+ *   residual, gamma, eps, residual_out, norm_out, workspace, workspace_bytes
+ *                  as in moe_finalize_rmsnorm_run (outputs may not overlap rank_partials).
+ */
+int moe_rank_sum_rmsnorm_run(const void* rank_partials, int world_size, const void* residual,
+                             const void* gamma, float eps, void* residual_out, void* norm_out,
+                             void* workspace, size_t workspace_bytes, int64_t num_tokens,
+                             int64_t hidden, int act_dtype, void* stream);
+
+/*
+ * moe_rank_sum_quant_run -- moe_rank_sum_rmsnorm_run followed by the NVFP4 / FP8 quantization of
+ * moe_finalize_quant_run (same arguments and conventions as there; norm_out nullable).
+ */
+int moe_rank_sum_quant_run(const void* rank_partials, int world_size, const void* residual,
+                           const void* gamma, float eps, int quant_type, const float* quant_scale,
+                           void* quant_out, void* scale_out, int sf_layout, void* residual_out,
+                           void* norm_out, void* workspace, size_t workspace_bytes,
+                           int64_t num_tokens, int64_t hidden, int act_dtype, void* stream);
+
+/*
  * moe_finalize_sf_size -- bytes of the NVFP4 block-scale buffer for a [num_tokens, hidden]
  * output: SWIZZLED_128x4 pads rows to a multiple of 128 and blocks per row to a multiple of 4,
  * roundup(T,128) * roundup(H/16,4) ([FI6631] test changes: T*H/16 bytes is too small and was

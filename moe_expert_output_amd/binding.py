@@ -23,7 +23,8 @@ MOE_SF_LINEAR, MOE_SF_SWIZZLED_128x4 = 0, 1
 EXPORTED = ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_run",
             "moe_finalize_sf_size", "moe_finalize_error_string", "moe_finalize_version",
             "moe_finalize_launch_floor_run", "moe_finalize_workspace_size", "moe_quantize_run",
-            "moe_residual_rmsnorm_run", "moe_finalize_stream_floor_run")
+            "moe_residual_rmsnorm_run", "moe_finalize_stream_floor_run",
+            "moe_rank_sum_rmsnorm_run", "moe_rank_sum_quant_run")
 
 _ACT = {torch.bfloat16: MOE_DTYPE_BF16, torch.float16: MOE_DTYPE_FP16}
 _SCALE = {torch.float32: MOE_DTYPE_FP32, torch.bfloat16: MOE_DTYPE_BF16}
@@ -65,6 +66,12 @@ def _load() -> ctypes.CDLL:
     lib.moe_finalize_launch_floor_run.restype = ctypes.c_int
     lib.moe_finalize_stream_floor_run.argtypes = [vp, sz, vp, sz, vp]
     lib.moe_finalize_stream_floor_run.restype = ctypes.c_int
+    lib.moe_rank_sum_rmsnorm_run.argtypes = [vp, i32, vp, vp, f32, vp, vp, vp, sz, i64, i64, i32,
+                                             vp]
+    lib.moe_rank_sum_rmsnorm_run.restype = ctypes.c_int
+    lib.moe_rank_sum_quant_run.argtypes = [vp, i32, vp, vp, f32, i32, vp, vp, vp, i32, vp, vp, vp,
+                                           sz, i64, i64, i32, vp]
+    lib.moe_rank_sum_quant_run.restype = ctypes.c_int
     return lib
 
 
@@ -212,3 +219,35 @@ def moe_residual_rmsnorm_run(x: torch.Tensor, residual: torch.Tensor, gamma: tor
     _check(LIB.moe_residual_rmsnorm_run(_ptr(x), _ptr(residual), _ptr(gamma), float(eps),
                                         _ptr(residual_out), _ptr(norm_out), wp, wb, T, H,
                                         _ACT[x.dtype], _stream(x, stream)))
+
+
+def moe_rank_sum_rmsnorm_run(rank_partials: torch.Tensor, residual: torch.Tensor,
+                             gamma: torch.Tensor, eps: float, residual_out: Optional[torch.Tensor],
+                             norm_out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> None:
+    """rank_partials: [world_size, T, H]."""
+    if rank_partials.dtype not in _ACT:
+        raise ValueError(f"activation dtype {rank_partials.dtype} is not bf16/fp16")
+    W, T, H = rank_partials.shape
+    wp, wb = _ws(workspace)
+    _check(LIB.moe_rank_sum_rmsnorm_run(_ptr(rank_partials), W, _ptr(residual), _ptr(gamma),
+                                        float(eps), _ptr(residual_out), _ptr(norm_out), wp, wb, T,
+                                        H, _ACT[rank_partials.dtype], _stream(residual, stream)))
+
+
+def moe_rank_sum_quant_run(rank_partials: torch.Tensor, residual: torch.Tensor,
+                           gamma: torch.Tensor, eps: float, quant_type: int,
+                           quant_scale: torch.Tensor, quant_out: torch.Tensor,
+                           scale_out: Optional[torch.Tensor], sf_layout: int,
+                           residual_out: Optional[torch.Tensor], norm_out: Optional[torch.Tensor],
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """rank_partials: [world_size, T, H]."""
+    if rank_partials.dtype not in _ACT:
+        raise ValueError(f"activation dtype {rank_partials.dtype} is not bf16/fp16")
+    W, T, H = rank_partials.shape
+    wp, wb = _ws(workspace)
+    _check(LIB.moe_rank_sum_quant_run(_ptr(rank_partials), W, _ptr(residual), _ptr(gamma),
+                                      float(eps), int(quant_type), _ptr(quant_scale),
+                                      _ptr(quant_out), _ptr(scale_out), int(sf_layout),
+                                      _ptr(residual_out), _ptr(norm_out), wp, wb, T, H,
+                                      _ACT[rank_partials.dtype], _stream(residual, stream)))

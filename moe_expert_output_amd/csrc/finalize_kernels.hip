@@ -63,7 +63,7 @@ struct Params {
   int slot_span;             // slots covered by one workgroup (L * P)
   int slices;                // workgroups per token (> 1: the row is split, see below)
   uint8_t* ws;               // workspace of the split row modes (null when slices == 1)
-  int identity_routes;       // 1: no route map, token t's single route is row t (K = 1)
+  int route_stride;          // > 0: no route map; route k of token t is row k * route_stride + t
 };
 
 // Split rows. When a token's row is spread over `slices` workgroups, each workgroup publishes
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   const int lane64 = tid & 63;
   const bool bf16_scales = a.scales_bf16 != 0;
   const uint32_t my_idx = __builtin_amdgcn_raw_buffer_load_b32(
-      rsrc(a.idx + (int64_t)t * a.K, a.identity_routes ? 0u : (uint32_t)a.K * 4u),
+      rsrc(a.idx + (int64_t)t * a.K, a.route_stride ? 0u : (uint32_t)a.K * 4u),
       (uint32_t)lane64 * 4u, 0, 0);
   // Raw scale bits of both formats; the unused (or missing) one has an empty buffer. Loads are
   // predicated by buffer size, never by branches: a branch join makes the compiler wait for
@@ -271,7 +271,8 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     for (int jj = 0; jj < CH; ++jj) {
       const int k = g + (c0 + jj) * G;
       const int kk = k < a.K ? k : 0;
-      const int pidx = a.identity_routes ? t : __builtin_amdgcn_readlane((int)my_idx, kk);
+      const int pidx =
+          a.route_stride ? kk * a.route_stride + t : __builtin_amdgcn_readlane((int)my_idx, kk);
       present[jj] = k < a.K && (uint32_t)pidx < (uint32_t)a.n_rows;
       const uint32_t wbits = (uint32_t)__builtin_amdgcn_readlane((int)my_wbits, kk);
       // an absent route's scale is never used: its weight is 0 (and its row reads zeros)
@@ -715,7 +716,7 @@ static size_t workspace_bytes_for(int64_t T) { return kWsHeader + (size_t)T * kW
 static int run_rows(int mode, const Common& c, const void* residual, const void* gamma,
                     float eps, void* residual_out, void* norm_out, const float* qscale,
                     void* quant_out, void* scale_out, int sf_layout, void* workspace,
-                    void* stream, bool identity_routes = false) {
+                    void* stream, int route_stride = 0) {
   const int slices = workspace ? choose_slices(c.T, (int)(c.H / 8)) : 1;
   Config cfg;
   if (!make_config(mode, c.T, (int)c.H, c.K, slices, &cfg)) return MOE_FIN_ERR_HIDDEN;
@@ -735,7 +736,7 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
   p.slot_span = cfg.span;
   p.slices = cfg.grid_x;
   p.ws = (uint8_t*)workspace;
-  p.identity_routes = identity_routes ? 1 : 0;
+  p.route_stride = route_stride;
   hipStream_t s = (hipStream_t)stream;
   switch (mode) {
     case MODE_RMS: return to_code(dispatch<MODE_RMS>(c.act, p, cfg, s));
@@ -783,13 +784,90 @@ static int check_workspace(const Common& c, const void* ws, size_t ws_bytes,
   return MOE_FIN_OK;
 }
 
+// The residual + RMSNorm entry points after their own shape checks: rows (with a route map,
+// route_stride == 0) or strided rows (route_stride = T: route k of token t is row k*T + t, no map).
+static int rmsnorm_call(const Common& c, const void* residual, const void* gamma, float eps,
+                        void* residual_out, void* norm_out, void* workspace,
+                        size_t workspace_bytes, void* stream, int route_stride) {
+  if (c.H > 16384) return MOE_FIN_ERR_HIDDEN;
+  if (c.T == 0) return MOE_FIN_OK;
+  int rc;
+  if (route_stride == 0) {
+    if ((rc = check_pointers(c))) return rc;
+  } else {
+    if (!c.rows) return MOE_FIN_ERR_NULL_POINTER;
+    if (!aligned(c.rows, 16)) return MOE_FIN_ERR_ALIGNMENT;
+  }
+  if ((rc = check_rows(c, residual, gamma, residual_out, norm_out, true))) return rc;
+  const size_t tb = (size_t)c.T * c.H * 2;
+  if ((rc = check_workspace(c, workspace, workspace_bytes,
+                            {rng(residual, tb), rng(gamma, (size_t)c.H * 2),
+                             residual_out ? rng(residual_out, tb) : Range{0, 0},
+                             rng(norm_out, tb)})))
+    return rc;
+  return run_rows(MODE_RMS, c, residual, gamma, eps, residual_out, norm_out, nullptr, nullptr,
+                  nullptr, 0, workspace, stream, route_stride);
+}
+
+// The quantized entry points, likewise.
+static int quant_call(const Common& c, const void* residual, const void* gamma, float eps,
+                      int quant_type, const float* quant_scale, void* quant_out, void* scale_out,
+                      int sf_layout, void* residual_out, void* norm_out, void* workspace,
+                      size_t workspace_bytes, void* stream, int route_stride) {
+  if (quant_type != MOE_QUANT_NVFP4 && quant_type != MOE_QUANT_FP8_E4M3)
+    return MOE_FIN_ERR_QUANT_TYPE;
+  const bool nvfp4 = quant_type == MOE_QUANT_NVFP4;
+  if (nvfp4 && sf_layout != MOE_SF_LINEAR && sf_layout != MOE_SF_SWIZZLED_128x4)
+    return MOE_FIN_ERR_SF_LAYOUT;
+  int rc = check_common(c, nvfp4 ? 16 : 8);
+  if (rc) return rc;
+  if (c.H > 16384) return MOE_FIN_ERR_HIDDEN;
+  if (c.T == 0) return MOE_FIN_OK;
+  if (route_stride == 0) {
+    if ((rc = check_pointers(c))) return rc;
+  } else {
+    if (!c.rows) return MOE_FIN_ERR_NULL_POINTER;
+    if (!aligned(c.rows, 16)) return MOE_FIN_ERR_ALIGNMENT;
+  }
+  if ((rc = check_rows(c, residual, gamma, residual_out, norm_out, false))) return rc;
+  if (!quant_scale || !quant_out || (nvfp4 && !scale_out)) return MOE_FIN_ERR_NULL_POINTER;
+  if (!aligned(quant_scale, 4) || !aligned(quant_out, 16) || (nvfp4 && !aligned(scale_out, 4)))
+    return MOE_FIN_ERR_ALIGNMENT;
+  const size_t qbytes = (size_t)c.T * c.H / (nvfp4 ? 2 : 1);
+  const size_t sbytes = nvfp4 ? moe_finalize_sf_size(c.T, c.H, sf_layout) : 0;
+  const size_t tb = (size_t)c.T * c.H * 2;
+  Range q = rng(quant_out, qbytes);
+  if (inputs_overlap(c, q) || overlap(q, rng(residual, tb)) ||
+      overlap(q, rng(gamma, (size_t)c.H * 2)) ||
+      (residual_out && overlap(q, rng(residual_out, tb))) ||
+      (norm_out && overlap(q, rng(norm_out, tb))) || overlap(q, rng(quant_scale, 4)))
+    return MOE_FIN_ERR_ALIAS;
+  if (nvfp4) {
+    Range sr = rng(scale_out, sbytes);
+    if (inputs_overlap(c, sr) || overlap(sr, q) || overlap(sr, rng(residual, tb)) ||
+        overlap(sr, rng(gamma, (size_t)c.H * 2)) ||
+        (residual_out && overlap(sr, rng(residual_out, tb))) ||
+        (norm_out && overlap(sr, rng(norm_out, tb))) || overlap(sr, rng(quant_scale, 4)))
+      return MOE_FIN_ERR_ALIAS;
+  }
+  if ((rc = check_workspace(c, workspace, workspace_bytes,
+                            {rng(residual, tb), rng(gamma, (size_t)c.H * 2),
+                             residual_out ? rng(residual_out, tb) : Range{0, 0},
+                             norm_out ? rng(norm_out, tb) : Range{0, 0}, q,
+                             nvfp4 ? rng(scale_out, sbytes) : Range{0, 0},
+                             rng(quant_scale, 4)})))
+    return rc;
+  return run_rows(nvfp4 ? MODE_NVFP4 : MODE_FP8, c, residual, gamma, eps, residual_out, norm_out,
+                  quant_scale, quant_out, scale_out, sf_layout, workspace, stream, route_stride);
+}
+
 }  // namespace mfin
 
 using namespace mfin;
 
 extern "C" {
 
-int moe_finalize_version(void) { return 100; }
+int moe_finalize_version(void) { return 200; }
 
 const char* moe_finalize_error_string(int code) {
   switch (code) {
@@ -902,20 +980,10 @@ int moe_finalize_rmsnorm_run(const void* permuted_rows, int64_t num_permuted_row
   Common c{permuted_rows, num_permuted_rows, expanded_idx_to_permuted_idx, expert_scales,
            scales_dtype, shared_expert_output, routed_scaling_factor, num_tokens, hidden,
            top_k, act_dtype};
-  int rc = check_common(c, 8);
+  const int rc = check_common(c, 8);
   if (rc) return rc;
-  if (hidden > 16384) return MOE_FIN_ERR_HIDDEN;
-  if (num_tokens == 0) return MOE_FIN_OK;
-  if ((rc = check_pointers(c))) return rc;
-  if ((rc = check_rows(c, residual, gamma, residual_out, norm_out, true))) return rc;
-  const size_t tb = (size_t)num_tokens * hidden * 2;
-  if ((rc = check_workspace(c, workspace, workspace_bytes,
-                            {rng(residual, tb), rng(gamma, (size_t)hidden * 2),
-                             residual_out ? rng(residual_out, tb) : Range{0, 0},
-                             rng(norm_out, tb)})))
-    return rc;
-  return run_rows(MODE_RMS, c, residual, gamma, eps, residual_out, norm_out, nullptr, nullptr,
-                  nullptr, 0, workspace, stream);
+  return rmsnorm_call(c, residual, gamma, eps, residual_out, norm_out, workspace,
+                      workspace_bytes, stream, 0);
 }
 
 int moe_residual_rmsnorm_run(const void* x, const void* residual, const void* gamma, float eps,
@@ -926,21 +994,36 @@ int moe_residual_rmsnorm_run(const void* x, const void* residual, const void* ga
   // token (row t of x, weight 1), RSF 1 and no shared term reproduces x exactly.
   Common c{x, num_tokens, nullptr, nullptr, MOE_DTYPE_FP32, nullptr, 1.0f, num_tokens, hidden,
            1, act_dtype};
-  int rc = check_common(c, 8);
+  const int rc = check_common(c, 8);
   if (rc) return rc;
-  if (hidden > 16384) return MOE_FIN_ERR_HIDDEN;
-  if (num_tokens == 0) return MOE_FIN_OK;
-  if (!x) return MOE_FIN_ERR_NULL_POINTER;
-  if (!aligned(x, 16)) return MOE_FIN_ERR_ALIGNMENT;
-  if ((rc = check_rows(c, residual, gamma, residual_out, norm_out, true))) return rc;
-  const size_t tb = (size_t)num_tokens * hidden * 2;
-  if ((rc = check_workspace(c, workspace, workspace_bytes,
-                            {rng(residual, tb), rng(gamma, (size_t)hidden * 2),
-                             residual_out ? rng(residual_out, tb) : Range{0, 0},
-                             rng(norm_out, tb)})))
-    return rc;
-  return run_rows(MODE_RMS, c, residual, gamma, eps, residual_out, norm_out, nullptr, nullptr,
-                  nullptr, 0, workspace, stream, /*identity_routes=*/true);
+  return rmsnorm_call(c, residual, gamma, eps, residual_out, norm_out, workspace,
+                      workspace_bytes, stream, (int)num_tokens);
+}
+
+int moe_rank_sum_rmsnorm_run(const void* rank_partials, int world_size, const void* residual,
+                             const void* gamma, float eps, void* residual_out, void* norm_out,
+                             void* workspace, size_t workspace_bytes, int64_t num_tokens,
+                             int64_t hidden, int act_dtype, void* stream) {
+  // The rank sum is the finalize with one route per rank (row r*T + t, weight 1), RSF 1 and no
+  // shared term: the float32 sum of the W partials, rounded once.
+  Common c{rank_partials, (int64_t)world_size * num_tokens, nullptr, nullptr, MOE_DTYPE_FP32,
+           nullptr, 1.0f, num_tokens, hidden, world_size, act_dtype};
+  const int rc = check_common(c, 8);
+  if (rc) return rc;
+  return rmsnorm_call(c, residual, gamma, eps, residual_out, norm_out, workspace,
+                      workspace_bytes, stream, (int)num_tokens);
+}
+
+int moe_rank_sum_quant_run(const void* rank_partials, int world_size, const void* residual,
+                           const void* gamma, float eps, int quant_type, const float* quant_scale,
+                           void* quant_out, void* scale_out, int sf_layout, void* residual_out,
+                           void* norm_out, void* workspace, size_t workspace_bytes,
+                           int64_t num_tokens, int64_t hidden, int act_dtype, void* stream) {
+  Common c{rank_partials, (int64_t)world_size * num_tokens, nullptr, nullptr, MOE_DTYPE_FP32,
+           nullptr, 1.0f, num_tokens, hidden, world_size, act_dtype};
+  return quant_call(c, residual, gamma, eps, quant_type, quant_scale, quant_out, scale_out,
+                    sf_layout, residual_out, norm_out, workspace, workspace_bytes, stream,
+                    (int)num_tokens);
 }
 
 int moe_quantize_run(const void* x, int64_t num_tokens, int64_t hidden, int act_dtype,
@@ -1002,46 +1085,8 @@ int moe_finalize_quant_run(const void* permuted_rows, int64_t num_permuted_rows,
   Common c{permuted_rows, num_permuted_rows, expanded_idx_to_permuted_idx, expert_scales,
            scales_dtype, shared_expert_output, routed_scaling_factor, num_tokens, hidden,
            top_k, act_dtype};
-  if (quant_type != MOE_QUANT_NVFP4 && quant_type != MOE_QUANT_FP8_E4M3)
-    return MOE_FIN_ERR_QUANT_TYPE;
-  const bool nvfp4 = quant_type == MOE_QUANT_NVFP4;
-  if (nvfp4 && sf_layout != MOE_SF_LINEAR && sf_layout != MOE_SF_SWIZZLED_128x4)
-    return MOE_FIN_ERR_SF_LAYOUT;
-  int rc = check_common(c, nvfp4 ? 16 : 8);
-  if (rc) return rc;
-  if (hidden > 16384) return MOE_FIN_ERR_HIDDEN;
-  if (num_tokens == 0) return MOE_FIN_OK;
-  if ((rc = check_pointers(c))) return rc;
-  if ((rc = check_rows(c, residual, gamma, residual_out, norm_out, false))) return rc;
-  if (!quant_scale || !quant_out || (nvfp4 && !scale_out)) return MOE_FIN_ERR_NULL_POINTER;
-  if (!aligned(quant_scale, 4) || !aligned(quant_out, 16) || (nvfp4 && !aligned(scale_out, 4)))
-    return MOE_FIN_ERR_ALIGNMENT;
-  const size_t qbytes = (size_t)num_tokens * hidden / (nvfp4 ? 2 : 1);
-  const size_t sbytes = nvfp4 ? moe_finalize_sf_size(num_tokens, hidden, sf_layout) : 0;
-  const size_t tb = (size_t)num_tokens * hidden * 2;
-  Range q = rng(quant_out, qbytes);
-  if (inputs_overlap(c, q) || overlap(q, rng(residual, tb)) ||
-      overlap(q, rng(gamma, (size_t)hidden * 2)) ||
-      (residual_out && overlap(q, rng(residual_out, tb))) ||
-      (norm_out && overlap(q, rng(norm_out, tb))) || overlap(q, rng(quant_scale, 4)))
-    return MOE_FIN_ERR_ALIAS;
-  if (nvfp4) {
-    Range sr = rng(scale_out, sbytes);
-    if (inputs_overlap(c, sr) || overlap(sr, q) || overlap(sr, rng(residual, tb)) ||
-        overlap(sr, rng(gamma, (size_t)hidden * 2)) ||
-        (residual_out && overlap(sr, rng(residual_out, tb))) ||
-        (norm_out && overlap(sr, rng(norm_out, tb))) || overlap(sr, rng(quant_scale, 4)))
-      return MOE_FIN_ERR_ALIAS;
-  }
-  if ((rc = check_workspace(c, workspace, workspace_bytes,
-                            {rng(residual, tb), rng(gamma, (size_t)hidden * 2),
-                             residual_out ? rng(residual_out, tb) : Range{0, 0},
-                             norm_out ? rng(norm_out, tb) : Range{0, 0}, q,
-                             nvfp4 ? rng(scale_out, sbytes) : Range{0, 0},
-                             rng(quant_scale, 4)})))
-    return rc;
-  return run_rows(nvfp4 ? MODE_NVFP4 : MODE_FP8, c, residual, gamma, eps, residual_out, norm_out,
-                  quant_scale, quant_out, scale_out, sf_layout, workspace, stream);
+  return quant_call(c, residual, gamma, eps, quant_type, quant_scale, quant_out, scale_out,
+                    sf_layout, residual_out, norm_out, workspace, workspace_bytes, stream, 0);
 }
 
 }  // extern "C"

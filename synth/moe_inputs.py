@@ -36,7 +36,7 @@ SCALE_DTYPES = {"fp32": torch.float32, "bf16": torch.bfloat16}
 # Seed bases per workload group. A case's seed is base + T (+ offsets for dtype / K variants), so
 # every case of every group has its own stream.
 _GROUP_BASE = {"tiny": 0, "decode": 1000, "larger": 2000, "highk": 3000, "quant": 4000,
-               "batch": 5000}
+               "batch": 5000, "ranksum": 6000}
 
 
 def workload_seed(group: str, T: int, act_dtype: str = "bf16", scale_dtype: str = "fp32",

@@ -185,3 +185,30 @@ def test_residual_rmsnorm_validation_codes():
     assert call(ws=WS + 64, wb=need) == -5
     assert call(ws=WS, wb=need - 1) == -11
     assert call(ws=X, wb=need) == -9
+
+
+def test_rank_sum_validation_codes():
+    f = LIB.moe_rank_sum_rmsnorm_run
+    P_, R, G, RO, NO = A, E, E + 0x100000, E + 0x200000, D
+
+    def call(p=P_, w=4, res=R, g=G, ro=RO, no=NO, ws=None, wb=0, T=4, H=1024, act=0):
+        return f(p, w, res, g, 1e-6, ro, no, ws, wb, T, H, act, None)
+
+    assert call(w=0) == -3 and call(w=65) == -3          # world size outside [1, 64]
+    assert call(act=3) == -6
+    assert call(H=1020) == -4 and call(H=16392) == -4
+    assert call(T=-1) == -2 and call(T=1 << 26, w=64) == -2   # world_size * T > 2^31 - 1
+    assert call(T=0) == 0 and call(T=0, p=None, res=None, g=None, no=None) == 0
+    assert call(p=None) == -1 and call(no=None) == -1 and call(res=None) == -1
+    assert call(p=P_ + 8) == -5 and call(ro=RO + 8) == -5
+    assert call(no=P_ + 4 * 4 * 1024 * 2 - 64) == -9      # overlaps the last partial row
+    need = M.moe_finalize_workspace_size(4, 1024, 4)
+    assert call(ws=WS, wb=need - 1) == -11
+    q = LIB.moe_rank_sum_quant_run
+    QS, QO, SO = E + 0x300000, E + 0x400000, E + 0x500000
+
+    def qcall(qt=1, layout=1, p=P_, w=4, so=SO, H=1024):
+        return q(p, w, R, G, 1e-6, qt, QS, QO, so, layout, RO, None, None, 0, 4, H, 0, None)
+
+    assert qcall(qt=0) == -7 and qcall(layout=2) == -8 and qcall(H=1032) == -4
+    assert qcall(w=0) == -3 and qcall(p=None) == -1 and qcall(so=None) == -1

@@ -808,3 +808,90 @@ def test_split_row_timeout_is_flagged_and_bounded():
     assert int(ws[:4].view(torch.int32).item()) == 0
     check_residual(np64(ro), ref, np64(inp.residual), "bf16")
     check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, "bf16")
+
+
+# ---- one GPU's share of the cross-rank reduction (moe_rank_sum_*_run) -----------------------------
+def _rank_sum_inputs(T, H, W, act, seed):
+    """W ranks' rounded finalize partials [W, T, H] (N(0,1) -> act), residual, gamma; expressed
+    as a finalize problem whose routes are the ranks (row r*T + t, weight 1, RSF 1, no shared),
+    which is how the oracle states the float32 rank sum rounded once."""
+    inp = make_inputs(T, H, W, act_dtype=act, seed=seed, mask_frac=0.0, scale_dtype=None,
+                      with_shared=False)
+    inp.idx = torch.arange(W, dtype=torch.int32).view(1, W) * T + \
+        torch.arange(T, dtype=torch.int32).view(T, 1)
+    inp.rsf = 1.0
+    return inp
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+@pytest.mark.parametrize("TWH", [(1, 4, 6144), (16, 4, 6144), (64, 4, 7168), (128, 4, 7168),
+                                 (128, 8, 7168), (5, 2, 1032), (3, 1, 48), (300, 8, 2048)])
+def test_rank_sum_rmsnorm(TWH, act):
+    T, W, H = TWH
+    inp = _rank_sum_inputs(T, H, W, act, seed=6000 + T + 10 * W)
+    _say(f"case rank_sum T={T} W={W} H={H} act={act} seed={inp.seed}")
+    ref = oracle_ref(inp)
+    parts = np64(inp.rows).reshape(W, T, H)
+    assert np.array_equal(O.rank_sum_rounded(list(parts), act), ref.s)   # the two oracle forms agree
+    P_ = inp.rows.view(W, T, H).cuda()
+    res, gam = inp.residual.cuda(), inp.gamma.cuda()
+    outs = []
+    for use_ws in (True, False):
+        ro = torch.empty(T, H, dtype=ACT_T[act], device="cuda")
+        no = torch.empty_like(ro)
+        M.moe_rank_sum_rmsnorm_run(P_, res, gam, inp.eps, ro, no, workspace(T) if use_ws else None)
+        torch.cuda.synchronize()
+        assert ws_flag() == 0
+        R, N = np64(ro), np64(no)
+        _say("  ", check_residual(R, ref, np64(inp.residual), act))
+        _say("  ", check_norm(N, R, ref, np64(inp.gamma), inp.eps, act))
+        outs.append(bits16(ro))
+    assert np.array_equal(outs[0], outs[1])          # residual_out does not depend on the split
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+def test_rank_sum_dyadic_bit_exact(act):
+    """Integer partials: the float32 rank sum is exact, so residual_out matches bit for bit."""
+    T, W, H = 33, 8, 2048
+    rng = np.random.Generator(np.random.PCG64(6100))
+    inp = _rank_sum_inputs(T, H, W, act, seed=6101)
+    inp.rows = torch.from_numpy(rng.integers(-64, 65, (W * T, H)).astype(np.float32)).to(ACT_T[act])
+    inp.residual = torch.from_numpy(rng.integers(-64, 65, (T, H)).astype(np.float32)).to(ACT_T[act])
+    ref = oracle_ref(inp)
+    ro = torch.empty(T, H, dtype=ACT_T[act], device="cuda")
+    no = torch.empty_like(ro)
+    M.moe_rank_sum_rmsnorm_run(inp.rows.view(W, T, H).cuda(), inp.residual.cuda(),
+                               inp.gamma.cuda(), inp.eps, ro, no, workspace(T))
+    torch.cuda.synchronize()
+    assert np.array_equal(np64(ro), ref.R)
+    check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, act)
+
+
+@pytest.mark.parametrize("qt", [M.MOE_QUANT_NVFP4, M.MOE_QUANT_FP8_E4M3])
+def test_rank_sum_quant(qt):
+    """Rank sum + residual + RMSNorm + quantization: codes and scales bit-exact against the
+    oracle's quantization of the kernel's own norm_out (which meets the norm_out bar)."""
+    T, W, H = 64, 4, 6144
+    inp = _rank_sum_inputs(T, H, W, "bf16", seed=6200)
+    ref = oracle_ref(inp)
+    P_ = inp.rows.view(W, T, H).cuda()
+    nv = qt == M.MOE_QUANT_NVFP4
+    scale = O.nvfp4_global_scale(ref.N) if nv else O.fp8_scale(ref.N)
+    qs = torch.tensor([scale], dtype=torch.float32, device="cuda")
+    ro = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    no = torch.empty_like(ro)
+    qo = torch.empty(T, H // 2 if nv else H, dtype=torch.uint8, device="cuda")
+    so = torch.empty(M.moe_finalize_sf_size(T, H, M.MOE_SF_SWIZZLED_128x4), dtype=torch.uint8,
+                     device="cuda") if nv else None
+    M.moe_rank_sum_quant_run(P_, inp.residual.cuda(), inp.gamma.cuda(), inp.eps, qt, qs, qo, so,
+                             M.MOE_SF_SWIZZLED_128x4, ro, no, workspace(T))
+    torch.cuda.synchronize()
+    R, N = np64(ro), np64(no)
+    check_residual(R, ref, np64(inp.residual), "bf16")
+    check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")
+    if nv:
+        want_c, want_s = O.quant_nvfp4(N, scale, M.MOE_SF_SWIZZLED_128x4)
+        assert np.array_equal(qo.cpu().numpy(), want_c)
+        assert np.array_equal(so.cpu().numpy(), want_s)
+    else:
+        assert np.array_equal(qo.cpu().numpy(), O.quant_fp8(N, scale))
