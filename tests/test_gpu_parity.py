@@ -895,3 +895,65 @@ def test_rank_sum_quant(qt):
         assert np.array_equal(so.cpu().numpy(), want_s)
     else:
         assert np.array_equal(qo.cpu().numpy(), O.quant_fp8(N, scale))
+
+
+def test_every_entry_point_replays_in_a_graph():
+    """Each entry point captured in a HIP graph (with the shared workspace where it takes one),
+    replayed three times with eager work and synchronizations between the replays: every replay
+    equals the eager call bit for bit (the workspace needs no reset between replays)."""
+    T, H, K = 48, 2048, 8
+    inp = make_inputs(T, H, K, seed=900)
+    d = to_dev(inp)
+    ws = torch.zeros(M.moe_finalize_workspace_size(T, H, K), dtype=torch.uint8, device="cuda")
+    qs_nv = torch.tensor([20.0], dtype=torch.float32, device="cuda")
+    qs_f8 = torch.tensor([30.0], dtype=torch.float32, device="cuda")
+    parts = torch.randn(4, T, H, device="cuda").to(torch.bfloat16)
+    x = torch.randn(T, H, device="cuda").to(torch.bfloat16)
+    bf = lambda: torch.empty(T, H, dtype=torch.bfloat16, device="cuda")  # noqa: E731
+    u8 = lambda n: torch.empty(n, dtype=torch.uint8, device="cuda")      # noqa: E731
+    sfb = M.moe_finalize_sf_size(T, H, M.MOE_SF_SWIZZLED_128x4)
+    o = {k: bf() for k in ("fin", "ro", "no", "qro", "rsro", "rsno", "rrro", "rrno")}
+    o.update(qnv=u8(T * H // 2).view(T, H // 2), sfnv=u8(sfb), qf8=u8(T * H).view(T, H),
+             qz=u8(T * H // 2).view(T, H // 2), sfz=u8(sfb))
+    calls = [
+        lambda s: M.moe_finalize_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                     o["fin"], stream=s),
+        lambda s: M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"],
+                                             inp.rsf, d["residual"], d["gamma"], inp.eps, o["ro"],
+                                             o["no"], ws, stream=s),
+        lambda s: M.moe_finalize_quant_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                           d["residual"], d["gamma"], inp.eps, M.MOE_QUANT_NVFP4,
+                                           qs_nv, o["qnv"], o["sfnv"], M.MOE_SF_SWIZZLED_128x4,
+                                           o["qro"], None, ws, stream=s),
+        lambda s: M.moe_finalize_quant_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                           d["residual"], d["gamma"], inp.eps,
+                                           M.MOE_QUANT_FP8_E4M3, qs_f8, o["qf8"], None, 0, None,
+                                           None, ws, stream=s),
+        lambda s: M.moe_rank_sum_rmsnorm_run(parts, d["residual"], d["gamma"], inp.eps, o["rsro"],
+                                             o["rsno"], ws, stream=s),
+        lambda s: M.moe_residual_rmsnorm_run(x, d["residual"], d["gamma"], inp.eps, o["rrro"],
+                                             o["rrno"], ws, stream=s),
+        lambda s: M.moe_quantize_run(x, M.MOE_QUANT_NVFP4, qs_nv, o["qz"], o["sfz"],
+                                     M.MOE_SF_SWIZZLED_128x4, stream=s),
+    ]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls:
+            c(s)
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in o.items()}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for c in calls:
+            c(s)
+    for rep in range(3):
+        for v in o.values():
+            v.zero_()
+        torch.randn(1 << 20, device="cuda").sum().item()      # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in o.items():
+            assert torch.equal(v, eager[k]), (rep, k)
+    assert int(ws[:4].view(torch.int32).item()) == 0
