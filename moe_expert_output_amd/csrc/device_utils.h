@@ -112,33 +112,48 @@ __device__ __forceinline__ float pair_max(float v) {
 }
 
 // --- exact-decision narrow encoders (inputs are exact FP64 magnitudes) -------------------------
+// Branch-free: every lane runs the same instruction stream, so the codes of a lane's 8 elements
+// are independent chains the compiler can interleave.
+//
 // OCP E4M3 ("fn"): bias 7, 3 mantissa bits, subnormals m * 2^-9, max 448. Round to nearest
-// even, saturate at 448. y >= 0, finite or NaN. Returns the 7-bit magnitude code.
+// even, saturate at 448. y >= 0, finite, infinite or NaN. Returns the 7-bit magnitude code.
 __device__ __forceinline__ uint32_t e4m3_code(double y) {
-  if (!(y == y)) return 0x7Fu;
-  if (y >= 448.0) return 0x7Eu;
-  if (y == 0.0) return 0u;
-  int e = __builtin_amdgcn_frexp_exp(y) - 1;  // y = m * 2^e, m in [1, 2)
-  e = e < -6 ? -6 : e;                        // below 2^-6 the spacing stays 2^-9 (subnormals)
-  double r = __builtin_rint(__builtin_amdgcn_ldexp(y, 3 - e));  // exact scale, RNE to integer
-  // normal: r in [8, 16]; subnormal: r in [0, 8]. A carry to 16 moves to the next binade.
-  return (uint32_t)((e + 7) * 8 + (int)r - 8);
+  const double yc = __builtin_fmin(y, 448.0);   // saturation (a NaN y is handled at the end)
+  // yc = m * 2^e with m in [1, 2); below 2^-6 (zero included) the spacing stays 2^-9
+  const int e = yc < 0x1p-6 ? -6 : __builtin_amdgcn_frexp_exp(yc) - 1;
+  const double r = __builtin_rint(__builtin_amdgcn_ldexp(yc, 3 - e));  // exact scale, RNE
+  // normal: r in [8, 16]; subnormal: r in [0, 8]. A carry to 16 moves to the next binade, and
+  // 448 itself gives 0x7E.
+  const uint32_t c = (uint32_t)((e + 7) * 8 + (int)r - 8);
+  return y == y ? c : 0x7Fu;
 }
 
 __device__ __forceinline__ double e4m3_value(uint32_t c) {
-  uint32_t ex = (c >> 3) & 0xFu, m = c & 7u;
-  if (ex == 0) return __builtin_amdgcn_ldexp((double)m, -9);
-  return __builtin_amdgcn_ldexp((double)(8 + m), (int)ex - 10);
+  const uint32_t ex = (c >> 3) & 0xFu, m = c & 7u;
+  const uint32_t mant = ex ? 8u + m : m;          // subnormal: m * 2^-9
+  const int sh = ex ? (int)ex - 10 : -9;          // normal: (8 + m) * 2^(ex - 10)
+  return __builtin_amdgcn_ldexp((double)mant, sh);
 }
 
-// E2M1 magnitude code of a*gs/sf given a_gs = |x| * gs (exact) and sf > 0: round to nearest
-// even among {0, .5, 1, 1.5, 2, 3, 4, 6} (codes 0..7), saturate at 6. Comparing a_gs against
-// midpoint*sf (exact products of narrow values) avoids any division.
+// Sign bit of d. A difference of two doubles is zero only when they are equal (gradual
+// underflow), so the sign of x - y decides x < y exactly.
+__device__ __forceinline__ uint32_t neg_bit(double d) {
+  return (uint32_t)(__builtin_bit_cast(uint64_t, d) >> 63);
+}
+
+// E2M1 magnitude code of a*gs/sf given a_gs = |x| * gs (exact) and sf >= 0: round to nearest
+// even among {0, .5, 1, 1.5, 2, 3, 4, 6} (codes 0..7), saturate at 6; 0 for NaN. Comparing a_gs
+// against midpoint*sf (exact products of narrow values) avoids any division. Each comparison is
+// the sign of one subtraction rather than a compare into VCC, so the seven tests of a lane's
+// eight elements are independent and overlap.
 __device__ __forceinline__ uint32_t e2m1_code(double a_gs, double sf) {
-  // ties to the even code: midpoints 0.25, 1.25, 2.5, 5 go down; 0.75, 1.75, 3.5 go up.
-  return (uint32_t)(a_gs > 0.25 * sf) + (uint32_t)(a_gs >= 0.75 * sf) +
-         (uint32_t)(a_gs > 1.25 * sf) + (uint32_t)(a_gs >= 1.75 * sf) +
-         (uint32_t)(a_gs > 2.5 * sf) + (uint32_t)(a_gs >= 3.5 * sf) + (uint32_t)(a_gs > 5.0 * sf);
+  // ties to the even code: midpoints 0.25, 1.25, 2.5, 5 go down (count a_gs > m * sf);
+  // 0.75, 1.75, 3.5 go up (count a_gs >= m * sf, i.e. 1 - [a_gs < m * sf])
+  const uint32_t above = neg_bit(0.25 * sf - a_gs) + neg_bit(1.25 * sf - a_gs) +
+                         neg_bit(2.5 * sf - a_gs) + neg_bit(5.0 * sf - a_gs);
+  const uint32_t below =
+      neg_bit(a_gs - 0.75 * sf) + neg_bit(a_gs - 1.75 * sf) + neg_bit(a_gs - 3.5 * sf);
+  return a_gs == a_gs ? above + 3u - below : 0u;
 }
 
 __device__ __forceinline__ uint32_t sign_bit(float x) {

@@ -125,11 +125,11 @@ __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
     amax = pair_max(amax);
     const uint32_t sfc = e4m3_code((double)amax * qs / 6.0);
     const double sf = e4m3_value(sfc);
+    const uint32_t keep = sfc != 0 ? 7u : 0u;    // a zero block scale gives zero codes
     uint32_t word = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint32_t m = 0;
-      if (sfc != 0) m = e2m1_code(__builtin_fabs((double)nr[e]) * qs, sf);
+      const uint32_t m = e2m1_code(__builtin_fabs((double)nr[e]) * qs, sf) & keep;
       word |= (m | (sign_bit(nr[e]) << 3)) << (4 * e);
     }
     __builtin_amdgcn_raw_buffer_store_b32(word, q_r, voff >> 2, 0, 0);
