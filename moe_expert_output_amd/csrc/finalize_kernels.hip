@@ -223,15 +223,20 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
       (uint32_t)lane64 * 2u, 0, 0);
   [[maybe_unused]] double qs = 0.0;
   if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) qs = (double)*a.qscale;
-  // Split rows: this slice's current epoch word, read now so the barrier does not wait for it.
-  // Every wavefront reads it unconditionally (from gamma, a valid dummy, when rows are whole):
-  // a load under a branch would make the compiler wait for it at the branch join.
-  [[maybe_unused]] uint64_t epoch_word = 0;
+  // Split rows: this slice's current epoch (the upper half of its exchange word), read now so the
+  // barrier does not wait for it. Every wavefront reads it unconditionally (from gamma, a valid
+  // dummy, when rows are whole): a load under a branch would make the compiler wait for it at the
+  // branch join. Only the 32 bits in use are loaded: with a 64-bit load the compiler reused the
+  // unused half's register at once, and that wait held the first row load back until this
+  // memory-side load had returned.
+  [[maybe_unused]] uint32_t epoch_prev = 0;
   if constexpr (MODE != MODE_FIN) {
-    const uint64_t* ep = a.slices > 1
-                             ? (const uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken) + slice
-                             : (const uint64_t*)a.gamma;
-    epoch_word = __hip_atomic_load(ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t* ep =
+        a.slices > 1
+            ? (const uint32_t*)((const uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken) +
+                                slice) + 1
+            : (const uint32_t*)a.gamma;
+    epoch_prev = __hip_atomic_load(ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // Group 0 also needs the shared-expert, residual and gamma slices; issue them alongside.
@@ -372,7 +377,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     if (a.slices > 1) {
       uint64_t* slot = (uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken);
       const int S = a.slices;
-      const uint32_t epoch = (uint32_t)(epoch_word >> 32) + 1u;
+      const uint32_t epoch = epoch_prev + 1u;
       const int m = slice + tid * S;              // this slice's slots
       if (m < kMaxSlices) {
         const uint64_t v = ((uint64_t)epoch << 32) |
