@@ -144,8 +144,10 @@ int moe_finalize_rmsnorm_run(const void* permuted_rows, int64_t num_permuted_row
  *   quant_scale  device pointer to ONE float32: the per-tensor global scale gs (NVFP4) or the
  *                FP8 scale s8. NVFP4: for every 16-element block of a row, sf = E4M3(gs*amax/6)
  *                and codes q = E2M1(x*gs/sf) (signed zeros when sf == 0). FP8: q = E4M3(x*s8).
- *                All conversions round to nearest even and saturate (E4M3 at 448, E2M1 at 6);
- *                the rounding decisions are exact (made in float64, where x*gs is exact).
+ *                All conversions round to nearest even and saturate (E4M3 at 448, E2M1 at 6;
+ *                infinities saturate too); the rounding decisions are exact (made in float64,
+ *                where x*gs is exact). Non-finite values: an FP8 NaN is 0x7F whatever its
+ *                sign; an NVFP4 block holding a NaN gets scale code 0x7F and all codes 0.
  *   quant_out    NVFP4: [num_tokens, hidden/2] bytes, element 2j in the low nibble of byte j.
  *                FP8:   [num_tokens, hidden] bytes.
  *   scale_out    NVFP4 only (else ignored, may be NULL): moe_finalize_sf_size(...) bytes of E4M3

@@ -113,24 +113,33 @@ __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
     u32x2 q = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t c = e4m3_code(__builtin_fabs((double)nr[e]) * qs) | (sign_bit(nr[e]) << 7);
+      // a NaN encodes as 0x7F whatever its sign bit
+      const uint32_t sgn = nr[e] == nr[e] ? sign_bit(nr[e]) : 0u;
+      const uint32_t c = e4m3_code(__builtin_fabs((double)nr[e]) * qs) | (sgn << 7);
       q[e >> 2] |= c << (8 * (e & 3));
     }
     __builtin_amdgcn_raw_buffer_store_b64(q, q_r, voff >> 1, 0, 0);
   } else {
     // NVFP4: a 16-element block is this lane's 8 elements and the neighbouring lane's 8.
-    float amax = 0.f;
+    // A NaN anywhere in the block makes its amax NaN: scale code 0x7F and all-zero codes.
+    float amax = 0.f, nan_here = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, __builtin_fabsf(nr[e]));
+    for (int e = 0; e < 8; ++e) {
+      amax = fmaxf(amax, __builtin_fabsf(nr[e]));
+      nan_here = nr[e] == nr[e] ? nan_here : 1.f;
+    }
     amax = pair_max(amax);
-    const uint32_t sfc = e4m3_code((double)amax * qs / 6.0);
+    const bool nan_blk = pair_max(nan_here) != 0.f;
+    const uint32_t sfc = nan_blk ? 0x7Fu : e4m3_code((double)amax * qs / 6.0);
     const double sf = e4m3_value(sfc);
-    const uint32_t keep = sfc != 0 ? 7u : 0u;    // a zero block scale gives zero codes
+    // a zero block scale gives signed zero codes; a NaN block gives zero codes without signs
+    const uint32_t keep = sfc != 0 && !nan_blk ? 7u : 0u;
+    const uint32_t sign_keep = nan_blk ? 0u : 1u;
     uint32_t word = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t m = e2m1_code(__builtin_fabs((double)nr[e]) * qs, sf) & keep;
-      word |= (m | (sign_bit(nr[e]) << 3)) << (4 * e);
+      word |= (m | ((sign_bit(nr[e]) & sign_keep) << 3)) << (4 * e);
     }
     __builtin_amdgcn_raw_buffer_store_b32(word, q_r, voff >> 2, 0, 0);
     // Scale bytes: lanes 8m..8m+7 hold blocks 4m'..4m'+3 (two lanes per block).

@@ -35,7 +35,7 @@ Why FP64 gives the exact rounding decisions here:
     because a real quotient that is not exactly a midpoint sits at least ~2^-35 (relative) away
     from it, while the FP64 division errs by at most 2^-53.
 
-Readings of points the pages leave open (each also listed in the design doc):
+Readings of points the pages leave open:
   R1  route validity: any index outside [0, n_rows) is an absent route; neither its row nor its
       scale is read ([FI6631] test changes: -1 routes; walkthrough: one bound check per route).
   R2  missing scales mean weight 1.0, missing shared output means 0, RSF 1.0 means "off"
@@ -45,6 +45,9 @@ Readings of points the pages leave open (each also listed in the design doc):
       all with round-to-nearest-even and saturation; even element in the low nibble; scale bytes
       in the SWIZZLED_128x4 layout with zero padding. FP8: q = E4M3(x * s8), saturating.
   R5  signed zero: values compare +0 == -0; quantized codes keep the sign bit of the input.
+  R7  non-finite values: an infinity saturates like any value above the largest finite code; a
+      NaN encodes as the E4M3 NaN code 0x7F (sign clear); a NaN in an NVFP4 block makes its
+      amax NaN, so the block scale byte is 0x7F and its codes are 0 (E2M1 has no NaN).
 """
 from __future__ import annotations
 

@@ -415,9 +415,9 @@ def test_quant_codec_edges():
 
 
 # ---- quantizing the oracle's rounded values: bit-exact everywhere ------------------------------
-def _quantize_dev(N_vals, act, qtype, qscale, layout):
-    T, H = N_vals.shape
-    x = torch.from_numpy(N_vals.astype(np.float32)).to(ACT_T[act]).cuda()   # exact: N is act-valued
+def _quantize_dev_x(x, qtype, qscale, layout):
+    """moe_quantize_run of the device tensor x; returns (codes, scale bytes or None)."""
+    T, H = x.shape
     nv = qtype == M.MOE_QUANT_NVFP4
     qo = torch.full((T, H // 2 if nv else H), 0xAB, dtype=torch.uint8, device="cuda")
     so = None
@@ -428,6 +428,11 @@ def _quantize_dev(N_vals, act, qtype, qscale, layout):
     M.moe_quantize_run(x, qtype, qs, qo, so, layout)
     torch.cuda.synchronize()
     return qo.cpu().numpy(), (None if so is None else so.cpu().numpy())
+
+
+def _quantize_dev(N_vals, act, qtype, qscale, layout):
+    x = torch.from_numpy(N_vals.astype(np.float32)).to(ACT_T[act]).cuda()   # exact: N is act-valued
+    return _quantize_dev_x(x, qtype, qscale, layout)
 
 
 @pytest.mark.parametrize("act", ["bf16", "fp16"])
@@ -541,6 +546,44 @@ def test_quantize_near_midpoints_bit_exact(act):
         want_c, want_s = O.quant_nvfp4(N3, gs2, 1)
         got_c, got_s = _quantize_dev(N3, act, M.MOE_QUANT_NVFP4, gs2, 1)
         assert np.array_equal(got_c, want_c) and np.array_equal(got_s, want_s), ("scale", draw)
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+def test_quantize_nonfinite_bit_exact(act):
+    """Infinities saturate (E4M3 448, E2M1 6); a NaN of either sign gives FP8 code 0x7F, and a
+    NaN anywhere in a 16-element block gives that block scale code 0x7F and all-zero codes, as
+    the oracle defines them. The tensor is built from bit patterns so NaN signs are exact."""
+    fmt = O.BF16 if act == "bf16" else O.FP16
+    rng = np.random.default_rng(91)
+    T, H = 3, 128
+    bits = O.encode_bits(_act_vals(rng.normal(size=(T, H)), act), fmt).astype(np.uint16)
+    inf_b, nan_b = (0x7F80, 0x7FC0) if act == "bf16" else (0x7C00, 0x7E00)
+    neg = 0x8000
+    bits[0, 20] = inf_b                      # block 1: +inf
+    bits[0, 40] = inf_b | neg                # block 2: -inf
+    bits[0, 60] = nan_b                      # block 3: +NaN
+    bits[1, 3] = nan_b | neg                 # block 0: -NaN next to an infinity
+    bits[1, 5] = inf_b
+    bits[1, 16:32] = 0                       # block 1: zeros, one of them -0
+    bits[1, 17] = neg
+    bits[2, 100] = nan_b | neg               # block 6: both NaN signs
+    bits[2, 101] = nan_b
+    N = O.decode_bits(bits, fmt)             # the values the kernel reads
+    x = torch.from_numpy(bits.view(np.int16)).view(ACT_T[act]).cuda()
+    finite_amax = float(np.max(np.abs(N[np.isfinite(N)])))
+    for layout in (M.MOE_SF_SWIZZLED_128x4, M.MOE_SF_LINEAR):
+        gs = float(np.float32(2688.0 / finite_amax))
+        want_c, want_s = O.quant_nvfp4(N, gs, layout)
+        got_c, got_s = _quantize_dev_x(x, M.MOE_QUANT_NVFP4, gs, layout)
+        assert np.array_equal(got_c, want_c), layout
+        assert np.array_equal(got_s, want_s), layout
+        assert want_s[O.sf_offset(0, 3, H, layout)] == 0x7F
+        assert want_s[O.sf_offset(0, 1, H, layout)] == 0x7E
+    s8 = float(np.float32(448.0 / finite_amax))
+    want = O.quant_fp8(N, s8)
+    got, _ = _quantize_dev_x(x, M.MOE_QUANT_FP8_E4M3, s8, 0)
+    assert np.array_equal(got, want)
+    assert want[1, 3] == 0x7F and want[2, 100] == 0x7F and want[0, 40] == 0xFE
 
 
 # ---- large batches (prefill-sized calls: whole rows, nontemporal streaming) ---------------------

@@ -136,3 +136,31 @@ def test_fp8_exact_bruteforce_and_saturation():
     assert list(c[0]) == [0x7E, 0xFE, 0x80, 0x00]
     # the tensor amax maps to 448
     assert np.max(np.abs(O.decode_bits(codes, O.E4M3))) == 448.0
+
+
+def test_nonfinite_inputs_follow_the_stated_reading():
+    """Non-finite values (the pages are silent): infinities saturate like any value above the
+    largest finite code; a NaN gives the E4M3 NaN code S.1111.111 with S = 0 whatever its sign;
+    an NVFP4 block holding a NaN has a NaN amax, hence a NaN block scale (code 0x7F) and NaN
+    ratios, which encode as E2M1 code 0 without sign. Finite blocks beside them are unaffected."""
+    inf, nan = np.inf, np.nan
+    fin = np.array([0.5, -1.5, 3.0, -0.25, 1.0, 2.0, -4.0, 0.75, 1.25, -0.5, 6.0, -3.0, 0.0, 1.75,
+                    -2.5, 0.125])
+    N = np.zeros((1, 64))
+    N[0, :16] = fin
+    N[0, 16:32] = fin
+    N[0, 16] = inf
+    N[0, 32:48] = fin
+    N[0, 33] = -nan
+    N[0, 48:64] = fin
+    N[0, 63] = -inf
+    gs = 1.0
+    codes, sf = O.quant_nvfp4(N, gs, O.SF_LINEAR)
+    c4 = _unpack(codes)[0]
+    ref_codes, ref_sf = O.quant_nvfp4(fin[None, :], gs, O.SF_LINEAR)
+    assert np.array_equal(c4[:16], _unpack(ref_codes)[0]) and sf[0] == ref_sf[0]
+    assert sf[1] == 0x7E and c4[16] == 0x7              # +inf: scale 448, code +6
+    assert sf[2] == 0x7F and not c4[32:48].any()        # NaN block: scale NaN, codes 0, no sign
+    assert sf[3] == 0x7E and c4[63] == 0xF              # -inf: code -6
+    q8 = O.quant_fp8(np.array([[inf, -inf, nan, -nan, 1.0, -0.0, 500.0, -500.0]]), 1.0)[0]
+    assert list(q8) == [0x7E, 0xFE, 0x7F, 0x7F, 0x38, 0x80, 0x7E, 0xFE]
