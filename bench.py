@@ -223,7 +223,8 @@ def main():
         "stream_ceiling_same_bytes_us": round(ceil_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "mfin::finalize_kernel<0, 1, 1, 1, 8> (bf16, RMSNorm, whole rows)",
+                     "kernel": "mfin::finalize_kernel<0, 1, 1, 1, 8, 2> (bf16, RMSNorm, whole rows, "
+                               "nontemporal streams)",
                      "per_launch_bytes": nbytes, "kernel_source_hash": kernel_source_hash(),
                      "stream_ceiling_GBs": round(nbytes / (ceil_us * 1e-6) / 1e9, 1),
                      "frac_of_stream_ceiling": round(ceil_us / us_per_call, 4)},
