@@ -291,6 +291,35 @@ def test_workspace_shared_across_shapes():
     assert ws_flag() == 0
 
 
+def test_concurrent_streams_with_own_workspaces():
+    """Split-row calls in flight on two streams at once, each stream with its own workspace (the
+    way to overlap calls; one workspace shared by overlapping calls would race): every result
+    equals the same call made alone, and neither workspace records a timeout."""
+    cases = [(16, 6144, 601), (64, 7168, 602), (1, 6144, 603), (32, 7168, 604), (4, 1024, 605),
+             (128, 7168, 606)]
+    inps = [make_inputs(T, H, 8, seed=sd) for T, H, sd in cases]
+    devs = [to_dev(i) for i in inps]
+    alone = [run_rmsnorm(i, d) for i, d in zip(inps, devs)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wss = [torch.zeros(M.moe_finalize_workspace_size(128, 7168, 8), dtype=torch.uint8,
+                       device="cuda") for _ in streams]
+    outs = [(torch.empty(i.T, i.H, dtype=torch.bfloat16, device="cuda"),
+             torch.empty(i.T, i.H, dtype=torch.bfloat16, device="cuda")) for i in inps]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    for _ in range(10):
+        for j, (i, d) in enumerate(zip(inps, devs)):
+            k = j % 2
+            with torch.cuda.stream(streams[k]):
+                M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], i.rsf,
+                                           d["residual"], d["gamma"], i.eps, outs[j][0],
+                                           outs[j][1], wss[k])
+    torch.cuda.synchronize()
+    for (ro, no), (ro1, no1) in zip(outs, alone):
+        assert np.array_equal(bits16(ro), bits16(ro1)) and np.array_equal(bits16(no), bits16(no1))
+    assert all(int(w[:4].view(torch.int32).item()) == 0 for w in wss)
+
+
 # ---- validation through the ABI on a device ---------------------------------------------------------
 def test_validation_errors():
     inp = make_inputs(4, 1024, 8, seed=304)
