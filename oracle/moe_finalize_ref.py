@@ -161,7 +161,8 @@ def decode_bits(bits, fmt: Fmt) -> np.ndarray:
     """Values of bit patterns of `fmt` (float64)."""
     bits = np.asarray(bits)
     if fmt is BF16:
-        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):      # signalling-NaN patterns widen to NaN
+            return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     if fmt is FP16:
         return bits.astype(np.uint16).view(np.float16).astype(np.float64)
     table = _TABLES[fmt.name]
