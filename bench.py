@@ -231,7 +231,8 @@ def main():
     }
     if a.sweep:
         out["cases"] = _sweep(torch, M, stream, dev, large=not a.no_large,
-                              groups=[g for g in a.groups.split(",") if g])
+                              groups=[g for g in a.groups.split(",") if g],
+                              cpu=not a.no_cpu_baseline)
     out["workspace_flag"] = int(ws[:4].view(torch.int32).item())
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, nbytes, a.cpu_seconds)
@@ -317,7 +318,7 @@ def _sweep_cases(large):
     return c
 
 
-def _sweep(torch, M, stream, dev, large=True, groups=()):
+def _sweep(torch, M, stream, dev, large=True, groups=(), cpu=False):
     """Every case: warm µs/call (the pages' protocol) and the launch floor; from T = 32 on also
     cold µs/call (inputs rotated over ROTATE_BYTES, up to MAX_SETS copies) and the streaming
     ceiling for the same bytes. GB/s use the fused path's algorithmic bytes (the two-kernel path's extra write and
@@ -426,8 +427,49 @@ def _sweep(torch, M, stream, dev, large=True, groups=()):
             del sets
         torch.cuda.empty_cache()
         rec["workspace_flag"] = int(ws_big[:4].view(torch.int32).item())
+        if cpu and entry in ("rmsnorm", "finalize", "rank_sum", "quant"):
+            qv = None if q_scale is None else float(q_scale.item())
+            o_us, o_runs = _oracle_case_us(inp, entry, qkind, qv)
+            rec.update({"oracle_us": round(o_us, 1), "oracle_runs": o_runs,
+                        "oracle_gbs": round(nb / (o_us * 1e-6) / 1e9, 4)})
         cases.append(rec)
     return cases
+
+
+def _oracle_case_us(inp, entry, qkind, q_scale):
+    """The FP64 oracle (unmodified) on this host, one thread, on the case's own inputs: one
+    warm-up call, then the median of 5 calls (2 when one call takes over a second)."""
+    import statistics
+
+    import oracle as O
+    f = lambda t: None if t is None else t.double().numpy()  # noqa: E731
+    rows, idx, sc, sh = f(inp.rows), inp.idx.numpy(), f(inp.scales), f(inp.shared)
+    res, gam = f(inp.residual), f(inp.gamma)
+
+    def call():
+        if entry == "finalize":
+            return O.finalize(rows, idx, sc, sh, inp.rsf, inp.act_dtype)
+        if entry == "rank_sum":
+            s = O.rank_sum_rounded(rows.reshape(inp.K, inp.T, inp.H), inp.act_dtype)
+            return O.residual_rmsnorm(s, res, gam, inp.eps, inp.act_dtype)
+        out = O.finalize_rmsnorm(rows, idx, sc, sh, inp.rsf, res, gam, inp.eps, inp.act_dtype)
+        if entry == "quant":
+            N = out[2]
+            if qkind == "fp8":
+                return O.quant_fp8(N, q_scale)
+            layout = O.SF_LINEAR if qkind == "nvfp4_linear" else O.SF_SWIZZLED_128x4
+            return O.quant_nvfp4(N, q_scale, layout)
+        return out
+
+    t0 = time.perf_counter()
+    call()
+    n = 2 if time.perf_counter() - t0 > 1.0 else 5
+    ts = []
+    for _ in range(n):
+        t0 = time.perf_counter()
+        call()
+        ts.append(time.perf_counter() - t0)
+    return statistics.median(ts) * 1e6, n
 
 
 def _dev_set(torch, inp, dev, qkind=""):
