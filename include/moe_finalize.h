@@ -268,6 +268,28 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
                                   void* stream);
 
 /*
+ * moe_finalize_launch_config -- the launch configuration entry point `entry` (0 =
+ * moe_finalize_run, 1 = moe_finalize_rmsnorm_run, 2 = moe_finalize_quant_run) chooses for a shape,
+ * with (with_workspace != 0) or without a workspace. Host-only, never touches the GPU. Writes
+ * MOE_FIN_LAUNCH_CONFIG_FIELDS int64 values to `out` (n_out is the caller's array length):
+ *   out[0] workgroups in the grid (0 when num_tokens == 0)
+ *   out[1] lanes per workgroup (route groups x lanes per group, a multiple of 64, <= 1024)
+ *   out[2] workgroups per token for the RMSNorm entries (slices of a split row; 1 = whole rows)
+ *   out[3] route groups G (wavefront groups that split top_k; partials combined in LDS)
+ *   out[4] 8-element slots per lane P
+ *   out[5] slots covered by one workgroup
+ *   out[6] dynamic LDS bytes
+ *   out[7] 1 when the streamed accesses are nontemporal (RMSNorm entries, >= 4 MiB of rows)
+ *   out[8] 1 when the library holds a kernel for this configuration
+ * Returns the entry point's shape-validation code (an unknown `entry` gives
+ * MOE_FIN_ERR_QUANT_TYPE), MOE_FIN_ERR_NULL_POINTER for out == NULL, MOE_FIN_ERR_BAD_SHAPE when
+ * n_out < MOE_FIN_LAUNCH_CONFIG_FIELDS.
+ */
+#define MOE_FIN_LAUNCH_CONFIG_FIELDS 9
+int moe_finalize_launch_config(int entry, int64_t num_tokens, int64_t hidden, int top_k,
+                               int with_workspace, int64_t* out, int n_out);
+
+/*
  * moe_finalize_stream_floor_run -- measurement aid: read `read_bytes` from `src` and write
  * `write_bytes` to `dst` in ONE kernel launch that does nothing else, the way an ideal finalize
  * would move its bytes (every 128-bit load of a lane issued before any is used, nontemporal loads

@@ -649,6 +649,19 @@ static hipError_t dispatch(int act, const Params& p, const Config& c, hipStream_
                                : dispatch_p<ACT_FP16, MODE>(p, c, s);
 }
 
+// Whether the dispatch above has a kernel instantiation for this configuration (the same
+// conditions as dispatch_p / dispatch_g / dispatch_j).
+static bool kernel_available(int mode, const Config& c) {
+  if (c.P != 1 && !(c.P == 2 && mode != MODE_FIN)) return false;
+  if (c.G != 1 && c.G != 2 && c.G != 4) return false;
+  switch (c.JMAX) {
+    case 4: case 8: case 16: return true;
+    case 32: return c.G <= 2;
+    case 64: return c.G == 1;
+  }
+  return false;
+}
+
 // ---- argument checks ----------------------------------------------------------------------------
 static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -920,20 +933,50 @@ size_t moe_finalize_workspace_size(int64_t num_tokens, int64_t hidden, int top_k
   return workspace_bytes_for(num_tokens);
 }
 
-int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden, int top_k,
-                                  void* stream) {
+// The launch configuration of entry point `entry` (0 = finalize, 1 = RMSNorm, 2 = quantized) for
+// one shape, with the entry point's own shape checks.
+static int entry_config(int entry, int64_t num_tokens, int64_t hidden, int top_k,
+                        bool with_workspace, Config* c) {
   if (entry < 0 || entry > 2) return MOE_FIN_ERR_QUANT_TYPE;
   if (top_k < 1 || top_k > 64) return MOE_FIN_ERR_BAD_TOPK;
   if (hidden <= 0 || hidden % 8 != 0 || (entry > 0 && hidden > 16384)) return MOE_FIN_ERR_HIDDEN;
   if (num_tokens < 0 || num_tokens > INT32_MAX / 2) return MOE_FIN_ERR_BAD_SHAPE;
-  if (num_tokens == 0) return MOE_FIN_OK;
+  const int64_t T = num_tokens > 0 ? num_tokens : 1;
+  const int slices = entry > 0 && with_workspace ? choose_slices(T, (int)(hidden / 8)) : 1;
+  if (!make_config(entry == 0 ? MODE_FIN : MODE_RMS, T, (int)hidden, top_k, slices, c))
+    return MOE_FIN_ERR_HIDDEN;
+  c->nontemporal = entry > 0 && use_nontemporal(T, hidden, top_k);
+  if ((int64_t)c->grid_x * T > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
+  return MOE_FIN_OK;
+}
+
+int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden, int top_k,
+                                  void* stream) {
   Config c;
-  make_config(entry == 0 ? MODE_FIN : MODE_RMS, num_tokens, (int)hidden, top_k,
-              entry == 0 ? 1 : choose_slices(num_tokens, (int)(hidden / 8)), &c);
-  if ((int64_t)c.grid_x * num_tokens > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
+  const int rc = entry_config(entry, num_tokens, hidden, top_k, true, &c);
+  if (rc || num_tokens == 0) return rc;
   hipLaunchKernelGGL(launch_floor_kernel, dim3((unsigned)(c.grid_x * num_tokens)), dim3(c.G * c.L),
                      c.lds, (hipStream_t)stream, 0);
   return to_code(hipGetLastError());
+}
+
+int moe_finalize_launch_config(int entry, int64_t num_tokens, int64_t hidden, int top_k,
+                               int with_workspace, int64_t* out, int n_out) {
+  if (!out) return MOE_FIN_ERR_NULL_POINTER;
+  if (n_out < MOE_FIN_LAUNCH_CONFIG_FIELDS) return MOE_FIN_ERR_BAD_SHAPE;
+  Config c;
+  const int rc = entry_config(entry, num_tokens, hidden, top_k, with_workspace != 0, &c);
+  if (rc) return rc;
+  out[0] = (int64_t)c.grid_x * num_tokens;
+  out[1] = (int64_t)c.G * c.L;
+  out[2] = entry > 0 ? c.grid_x : 1;
+  out[3] = c.G;
+  out[4] = c.P;
+  out[5] = c.span;
+  out[6] = (int64_t)c.lds;
+  out[7] = c.nontemporal ? 1 : 0;
+  out[8] = kernel_available(entry == 0 ? MODE_FIN : MODE_RMS, c) ? 1 : 0;
+  return MOE_FIN_OK;
 }
 
 int moe_finalize_stream_floor_run(const void* src, size_t read_bytes, void* dst,

@@ -41,6 +41,7 @@ def test_binding_constants_match_header():
     assert c["MOE_QUANT_FP8_E4M3"] == M.MOE_QUANT_FP8_E4M3
     assert c["MOE_SF_SWIZZLED_128x4"] == M.MOE_SF_SWIZZLED_128x4
     assert c["MOE_SF_LINEAR"] == M.MOE_SF_LINEAR
+    assert c["MOE_FIN_LAUNCH_CONFIG_FIELDS"] == len(M.LAUNCH_CONFIG_FIELDS)
 
 
 def test_error_strings():
@@ -212,3 +213,68 @@ def test_rank_sum_validation_codes():
 
     assert qcall(qt=0) == -7 and qcall(layout=2) == -8 and qcall(H=1032) == -4
     assert qcall(w=0) == -3 and qcall(p=None) == -1 and qcall(so=None) == -1
+
+
+def test_launch_config_validation_codes():
+    cfg = M.moe_finalize_launch_config
+    for args, code in [((3, 4, 1024, 8), M.MoeFinalizeError), ((1, 4, 1024, 0), M.MoeFinalizeError),
+                       ((1, 4, 1004, 8), M.MoeFinalizeError), ((1, 4, 16392, 8), M.MoeFinalizeError),
+                       ((1, -1, 1024, 8), M.MoeFinalizeError)]:
+        with pytest.raises(code):
+            cfg(*args)
+    L = M.LIB
+    out = (ctypes.c_int64 * 9)()
+    assert L.moe_finalize_launch_config(1, 4, 1024, 8, 1, None, 9) == -1
+    assert L.moe_finalize_launch_config(1, 4, 1024, 8, 1, out, 8) == -2
+    assert L.moe_finalize_launch_config(3, 4, 1024, 8, 1, out, 9) == -7
+    assert L.moe_finalize_launch_config(1, 4, 1024, 65, 1, out, 9) == -3
+    assert L.moe_finalize_launch_config(1, 4, 16392, 8, 1, out, 9) == -4
+    assert L.moe_finalize_launch_config(0, 4, 16392, 8, 0, out, 9) == 0   # finalize: any hidden
+    assert cfg(1, 0, 7168, 8)["workgroups"] == 0
+
+
+def test_launch_config_every_shape_has_a_kernel():
+    """Host logic over a sweep of shapes (tokens 1..4096, hidden 8..16384, top_k 1..64, every
+    entry kind, with and without a workspace): the chosen configuration has a compiled kernel, fits
+    one workgroup (whole wavefronts, <= 1024 lanes, <= 64 KiB LDS), gives every route group work,
+    covers each token's 8-element slots with non-empty slices, splits rows only within the slice
+    rule's bounds (<= hidden/512 slices, <= 224/T, <= 64; whole rows without a workspace), and
+    streams nontemporally exactly from 4 MiB of rows."""
+    Ts = [1, 2, 3, 4, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 112, 127, 128, 129, 224, 225,
+          256, 1000, 2048, 4096]
+    Hs = [8, 16, 48, 512, 520, 1000, 1024, 1032, 2048, 3584, 4096, 4104, 6144, 7168, 8192, 8200,
+          12288, 16376, 16384]
+    Ks = [1, 2, 3, 4, 5, 6, 8, 10, 16, 17, 22, 31, 32, 33, 63, 64]
+    n = 0
+    for entry in (0, 1, 2):
+        for ws in (False, True):
+            for T in Ts:
+                for H in Hs:
+                    nv = H // 8
+                    for K in Ks:
+                        c = M.moe_finalize_launch_config(entry, T, H, K, ws)
+                        n += 1
+                        where = (entry, ws, T, H, K, c)
+                        G, P, span = c["route_groups"], c["slots_per_lane"], c["slot_span"]
+                        assert c["kernel_available"] == 1, where
+                        assert c["lanes"] % 64 == 0 and 64 <= c["lanes"] <= 1024, where
+                        assert G in (1, 2, 4) and c["lanes"] % (64 * G) == 0, where
+                        assert G == 1 or G <= K, where               # every group has a route
+                        lanes_per_group = c["lanes"] // G
+                        assert P * lanes_per_group >= span, where
+                        assert c["lds_bytes"] == (G - 1) * P * lanes_per_group * 32, where
+                        assert c["lds_bytes"] <= 65536, where
+                        if entry == 0:
+                            assert span == 64 and P == 1, where
+                            assert c["workgroups"] == T * -(-nv // 64), where
+                            assert c["nontemporal"] == 0, where
+                            continue
+                        S = c["slices"]
+                        assert c["workgroups"] == T * S, where
+                        assert 1 <= S <= max(1, min(nv // 64, 224 // T, 64)), where
+                        if not ws:
+                            assert S == 1, where
+                        assert (S - 1) * span < nv <= S * span, where
+                        assert S == 1 or span % 8 == 0, where
+                        assert c["nontemporal"] == int(T * K * H * 2 >= 4 << 20), where
+    assert n == 3 * 2 * len(Ts) * len(Hs) * len(Ks)
