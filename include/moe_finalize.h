@@ -78,6 +78,7 @@ extern "C" {
 #define MOE_FIN_ERR_ALIAS (-9)          /* forbidden overlap between buffers                */
 #define MOE_FIN_ERR_HIP (-10)           /* the HIP runtime refused the launch               */
 #define MOE_FIN_ERR_WORKSPACE (-11)     /* workspace smaller than moe_finalize_workspace_size */
+#define MOE_FIN_ERR_POLICY (-12)        /* unknown cache policy                             */
 
 /* Element types. */
 #define MOE_DTYPE_BF16 0
@@ -279,13 +280,32 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
  *   out[4] 8-element slots per lane P
  *   out[5] slots covered by one workgroup
  *   out[6] dynamic LDS bytes
- *   out[7] 1 when the streamed accesses are nontemporal (RMSNorm entries, >= 4 MiB of rows)
+ *   out[7] 1 when the streamed accesses are nontemporal (see moe_finalize_set_cache_policy)
  *   out[8] 1 when the library holds a kernel for this configuration
  * Returns the entry point's shape-validation code (an unknown `entry` gives
  * MOE_FIN_ERR_QUANT_TYPE), MOE_FIN_ERR_NULL_POINTER for out == NULL, MOE_FIN_ERR_BAD_SHAPE when
  * n_out < MOE_FIN_LAUNCH_CONFIG_FIELDS.
  */
 #define MOE_FIN_LAUNCH_CONFIG_FIELDS 9
+
+/*
+ * moe_finalize_set_cache_policy -- how later calls of every entry point, from any thread, treat
+ * the tensors they stream (permuted rows, shared output and residual loads; residual_out and
+ * norm_out stores; gamma and the route metadata always stay cacheable):
+ *   MOE_FIN_CACHE_AUTO    (default) nontemporal from 4 MiB of permuted rows per call
+ *                         (num_tokens * top_k * hidden * 2 bytes), cacheable below;
+ *   MOE_FIN_CACHE_KEEP    always cacheable: for inputs that are already in the caches, or a
+ *                         pipeline whose next kernel reads residual_out / norm_out at once;
+ *   MOE_FIN_CACHE_STREAM  always nontemporal: for inputs that come from HBM.
+ * moe_finalize_run never stores its output nontemporally. Results are bit-identical under every
+ * policy. The policy is read when a call is enqueued, so a captured graph keeps the choice made
+ * at capture. Returns the previous policy, or MOE_FIN_ERR_POLICY for an unknown value (the
+ * policy is then unchanged). This is the library's only process-wide setting.
+ */
+#define MOE_FIN_CACHE_AUTO 0
+#define MOE_FIN_CACHE_KEEP 1
+#define MOE_FIN_CACHE_STREAM 2
+int moe_finalize_set_cache_policy(int policy);
 int moe_finalize_launch_config(int entry, int64_t num_tokens, int64_t hidden, int top_k,
                                int with_workspace, int64_t* out, int n_out);
 

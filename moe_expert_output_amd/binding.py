@@ -18,13 +18,15 @@ from .build_lib import LIB_PATH
 MOE_DTYPE_BF16, MOE_DTYPE_FP16, MOE_DTYPE_FP32 = 0, 1, 2
 MOE_QUANT_NVFP4, MOE_QUANT_FP8_E4M3 = 1, 2
 MOE_SF_LINEAR, MOE_SF_SWIZZLED_128x4 = 0, 1
+MOE_FIN_CACHE_AUTO, MOE_FIN_CACHE_KEEP, MOE_FIN_CACHE_STREAM = 0, 1, 2
 
 # Every symbol include/moe_finalize.h declares.
 EXPORTED = ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_run",
             "moe_finalize_sf_size", "moe_finalize_error_string", "moe_finalize_version",
             "moe_finalize_launch_floor_run", "moe_finalize_workspace_size", "moe_quantize_run",
             "moe_residual_rmsnorm_run", "moe_finalize_stream_floor_run",
-            "moe_rank_sum_rmsnorm_run", "moe_rank_sum_quant_run", "moe_finalize_launch_config")
+            "moe_rank_sum_rmsnorm_run", "moe_rank_sum_quant_run", "moe_finalize_launch_config",
+            "moe_finalize_set_cache_policy")
 
 _ACT = {torch.bfloat16: MOE_DTYPE_BF16, torch.float16: MOE_DTYPE_FP16}
 _SCALE = {torch.float32: MOE_DTYPE_FP32, torch.bfloat16: MOE_DTYPE_BF16}
@@ -67,6 +69,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_finalize_launch_config.argtypes = [i32, i64, i64, i32, i32,
                                                ctypes.POINTER(ctypes.c_int64), i32]
     lib.moe_finalize_launch_config.restype = ctypes.c_int
+    lib.moe_finalize_set_cache_policy.argtypes = [i32]
+    lib.moe_finalize_set_cache_policy.restype = ctypes.c_int
     lib.moe_finalize_stream_floor_run.argtypes = [vp, sz, vp, sz, vp]
     lib.moe_finalize_stream_floor_run.restype = ctypes.c_int
     lib.moe_rank_sum_rmsnorm_run.argtypes = [vp, i32, vp, vp, f32, vp, vp, vp, sz, i64, i64, i32,
@@ -126,6 +130,15 @@ def moe_finalize_launch_config(entry: int, num_tokens: int, hidden: int, top_k: 
                                           1 if with_workspace else 0, out,
                                           len(LAUNCH_CONFIG_FIELDS)))
     return dict(zip(LAUNCH_CONFIG_FIELDS, (int(v) for v in out)))
+
+
+def moe_finalize_set_cache_policy(policy: int) -> int:
+    """Set the process-wide cache policy for streamed tensors (MOE_FIN_CACHE_AUTO / _KEEP /
+    _STREAM); returns the previous one."""
+    prev = int(LIB.moe_finalize_set_cache_policy(int(policy)))
+    if prev < 0:
+        raise MoeFinalizeError(prev, moe_finalize_error_string(prev))
+    return prev
 
 
 def moe_finalize_stream_floor_run(src: torch.Tensor, read_bytes: int, dst: torch.Tensor,

@@ -30,6 +30,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <initializer_list>
 
 #include "../../include/moe_finalize.h"
@@ -519,9 +520,15 @@ struct Config {
 // Rows are read exactly once. Above 4 MiB of rows per call, nontemporal accesses to the streamed
 // tensors (row, shared and residual loads; residual_out and norm_out stores) measured 5-18 %
 // faster with the inputs in HBM (T = 64..256 at hidden 7168); below it they were no faster or
-// slower, so small calls keep cacheable accesses.
+// slower, so small calls keep cacheable accesses (MOE_FIN_CACHE_AUTO). The caller may override
+// the rule process-wide (moe_finalize_set_cache_policy); it is read when a call is enqueued.
 constexpr int64_t kNontemporalRowBytes = (int64_t)4 << 20;
+static std::atomic<int> g_cache_policy{MOE_FIN_CACHE_AUTO};
 static bool use_nontemporal(int64_t T, int64_t H, int K) {
+  switch (g_cache_policy.load(std::memory_order_relaxed)) {
+    case MOE_FIN_CACHE_KEEP: return false;
+    case MOE_FIN_CACHE_STREAM: return true;
+  }
   return T * (int64_t)K * H * 2 >= kNontemporalRowBytes;
 }
 
@@ -894,7 +901,14 @@ using namespace mfin;
 
 extern "C" {
 
-int moe_finalize_version(void) { return 200; }
+int moe_finalize_version(void) { return 201; }
+
+int moe_finalize_set_cache_policy(int policy) {
+  if (policy != MOE_FIN_CACHE_AUTO && policy != MOE_FIN_CACHE_KEEP &&
+      policy != MOE_FIN_CACHE_STREAM)
+    return MOE_FIN_ERR_POLICY;
+  return g_cache_policy.exchange(policy);
+}
 
 const char* moe_finalize_error_string(int code) {
   switch (code) {
@@ -913,6 +927,7 @@ const char* moe_finalize_error_string(int code) {
     case MOE_FIN_ERR_HIP: return "the HIP runtime refused the kernel launch";
     case MOE_FIN_ERR_WORKSPACE:
       return "workspace smaller than moe_finalize_workspace_size(num_tokens, hidden, top_k)";
+    case MOE_FIN_ERR_POLICY: return "unknown cache policy";
   }
   return "unknown error code";
 }
@@ -945,7 +960,7 @@ static int entry_config(int entry, int64_t num_tokens, int64_t hidden, int top_k
   const int slices = entry > 0 && with_workspace ? choose_slices(T, (int)(hidden / 8)) : 1;
   if (!make_config(entry == 0 ? MODE_FIN : MODE_RMS, T, (int)hidden, top_k, slices, c))
     return MOE_FIN_ERR_HIDDEN;
-  c->nontemporal = entry > 0 && use_nontemporal(T, hidden, top_k);
+  c->nontemporal = use_nontemporal(T, hidden, top_k);
   if ((int64_t)c->grid_x * T > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
   return MOE_FIN_OK;
 }

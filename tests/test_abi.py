@@ -42,6 +42,8 @@ def test_binding_constants_match_header():
     assert c["MOE_SF_SWIZZLED_128x4"] == M.MOE_SF_SWIZZLED_128x4
     assert c["MOE_SF_LINEAR"] == M.MOE_SF_LINEAR
     assert c["MOE_FIN_LAUNCH_CONFIG_FIELDS"] == len(M.LAUNCH_CONFIG_FIELDS)
+    assert (c["MOE_FIN_CACHE_AUTO"], c["MOE_FIN_CACHE_KEEP"], c["MOE_FIN_CACHE_STREAM"]) == (
+        M.MOE_FIN_CACHE_AUTO, M.MOE_FIN_CACHE_KEEP, M.MOE_FIN_CACHE_STREAM)
 
 
 def test_error_strings():
@@ -264,10 +266,10 @@ def test_launch_config_every_shape_has_a_kernel():
                         assert P * lanes_per_group >= span, where
                         assert c["lds_bytes"] == (G - 1) * P * lanes_per_group * 32, where
                         assert c["lds_bytes"] <= 65536, where
+                        assert c["nontemporal"] == int(T * K * H * 2 >= 4 << 20), where
                         if entry == 0:
                             assert span == 64 and P == 1, where
                             assert c["workgroups"] == T * -(-nv // 64), where
-                            assert c["nontemporal"] == 0, where
                             continue
                         S = c["slices"]
                         assert c["workgroups"] == T * S, where
@@ -276,5 +278,27 @@ def test_launch_config_every_shape_has_a_kernel():
                             assert S == 1, where
                         assert (S - 1) * span < nv <= S * span, where
                         assert S == 1 or span % 8 == 0, where
-                        assert c["nontemporal"] == int(T * K * H * 2 >= 4 << 20), where
     assert n == 3 * 2 * len(Ts) * len(Hs) * len(Ks)
+
+
+def test_cache_policy_setting():
+    """The process-wide cache policy: returns the previous value, rejects unknown ones without
+    changing anything, and decides the nontemporal choice every entry point reports."""
+    L = M.LIB
+    assert L.moe_finalize_set_cache_policy(M.MOE_FIN_CACHE_AUTO) == M.MOE_FIN_CACHE_AUTO
+    try:
+        big, small = (1, 128, 7168, 8), (1, 16, 6144, 8)
+        assert M.moe_finalize_launch_config(*big)["nontemporal"] == 1
+        assert M.moe_finalize_launch_config(*small)["nontemporal"] == 0
+        assert M.moe_finalize_set_cache_policy(M.MOE_FIN_CACHE_KEEP) == M.MOE_FIN_CACHE_AUTO
+        for e in (0, 1, 2):
+            assert M.moe_finalize_launch_config(e, 128, 7168, 8)["nontemporal"] == 0
+        assert L.moe_finalize_set_cache_policy(3) == -12 and L.moe_finalize_set_cache_policy(-1) == -12
+        with pytest.raises(M.MoeFinalizeError):
+            M.moe_finalize_set_cache_policy(7)
+        assert M.moe_finalize_set_cache_policy(M.MOE_FIN_CACHE_STREAM) == M.MOE_FIN_CACHE_KEEP
+        for e in (0, 1, 2):
+            assert M.moe_finalize_launch_config(e, 1, 1024, 1)["nontemporal"] == 1
+    finally:
+        M.moe_finalize_set_cache_policy(M.MOE_FIN_CACHE_AUTO)
+    assert M.moe_finalize_launch_config(*small)["nontemporal"] == 0

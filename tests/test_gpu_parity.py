@@ -320,6 +320,31 @@ def test_concurrent_streams_with_own_workspaces():
     assert all(int(w[:4].view(torch.int32).item()) == 0 for w in wss)
 
 
+@pytest.mark.parametrize("T,H", [(16, 6144), (64, 7168), (300, 3584)])
+def test_cache_policy_changes_no_bits(T, H):
+    """Every entry point gives bit-identical outputs under the three cache policies: cacheable or
+    nontemporal accesses change where data is cached, never what is computed."""
+    inp = make_inputs(T, H, 8, seed=700 + T)
+    d = to_dev(inp)
+    gs = O.nvfp4_global_scale(oracle_ref(inp).N)
+    pols = (M.MOE_FIN_CACHE_AUTO, M.MOE_FIN_CACHE_KEEP, M.MOE_FIN_CACHE_STREAM)
+    got = {}
+    prev = M.moe_finalize_set_cache_policy(M.MOE_FIN_CACHE_AUTO)
+    try:
+        for pol in pols:
+            M.moe_finalize_set_cache_policy(pol)
+            outs = [run_finalize(inp, d)]
+            outs += list(run_rmsnorm(inp, d)) + list(run_rmsnorm(inp, d, use_ws=False))
+            ro, no, qo, so = run_quant(inp, M.MOE_QUANT_NVFP4, gs)
+            got[pol] = [bits16(x) for x in outs + [ro, no]] + [np.asarray(qo), np.asarray(so)]
+    finally:
+        M.moe_finalize_set_cache_policy(prev)
+    for pol in pols[1:]:
+        for a, b in zip(got[pol], got[pols[0]]):
+            assert np.array_equal(a, b), pol
+    assert ws_flag() == 0
+
+
 # ---- validation through the ABI on a device ---------------------------------------------------------
 def test_validation_errors():
     inp = make_inputs(4, 1024, 8, seed=304)
