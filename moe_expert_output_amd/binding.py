@@ -171,20 +171,86 @@ def _stream(ref: torch.Tensor, stream) -> int:
     return torch.cuda.current_stream(ref.device).cuda_stream
 
 
-def _common(rows, idx, scales):
-    if rows.dtype not in _ACT:
-        raise ValueError(f"activation dtype {rows.dtype} is not bf16/fp16")
-    sdt = _SCALE.get(scales.dtype, -1) if scales is not None else MOE_DTYPE_FP32
+def _need(t: Optional[torch.Tensor], name: str, shape, dtype, optional: bool = False) -> None:
+    """Shape and dtype guard. The C ABI sees only pointers and the sizes passed beside them, so a
+    tensor smaller than the shape a call implies would be read or written past its end."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _need_bytes(t: Optional[torch.Tensor], name: str, nbytes: int, exact: bool) -> None:
+    if t is None:
+        return
+    have = t.numel() * t.element_size()
+    if (have != nbytes) if exact else (have < nbytes):
+        raise ValueError(f"{name} must hold {'exactly' if exact else 'at least'} {nbytes} bytes, "
+                         f"got {have}")
+
+
+def _act_dtype(t: torch.Tensor, name: str):
+    if t.dtype not in _ACT:
+        raise ValueError(f"{name}: activation dtype {t.dtype} is not bf16/fp16")
+    return t.dtype
+
+
+def _common(rows, idx, scales, shared, H):
+    """Route inputs of the finalize entry points: rows [N_rows, H], idx [T, K] int32, scales
+    [T, K] fp32 or bf16 (or None), shared [T, H] (or None), all activations of rows' dtype."""
+    dt = _act_dtype(rows, "permuted_rows")
+    if rows.dim() != 2 or idx.dim() != 2:
+        raise ValueError("permuted_rows must be [N_rows, H] and the index map [T, K]")
     T, K = idx.shape
-    return _ACT[rows.dtype], sdt, T, K
+    _need(rows, "permuted_rows", (rows.shape[0], H), dt)
+    _need(idx, "expanded_idx_to_permuted_idx", (T, K), torch.int32)
+    if scales is not None:
+        if scales.dtype not in _SCALE:
+            raise ValueError(f"expert_scales must be float32 or bfloat16, got {scales.dtype}")
+        _need(scales, "expert_scales", (T, K), scales.dtype)
+    _need(shared, "shared_expert_output", (T, H), dt, optional=True)
+    sdt = _SCALE[scales.dtype] if scales is not None else MOE_DTYPE_FP32
+    return _ACT[dt], sdt, T, K
+
+
+def _rows_out(dt, T, H, residual, gamma, residual_out, norm_out, norm_optional=False):
+    """The residual + RMSNorm tensors: residual, residual_out, norm_out [T, H]; gamma [H]."""
+    _need(residual, "residual", (T, H), dt)
+    _need(gamma, "gamma", (H,), dt)
+    _need(residual_out, "residual_out", (T, H), dt, optional=True)
+    _need(norm_out, "norm_out", (T, H), dt, optional=norm_optional)
+
+
+def _quant_out(T, H, quant_type, quant_scale, quant_out, scale_out, sf_layout):
+    """quant_scale: one float32; quant_out: T*H/2 (NVFP4) or T*H (FP8) bytes; scale_out (NVFP4):
+    at least moe_finalize_sf_size(T, H, sf_layout) bytes."""
+    if quant_scale is None or quant_scale.dtype != torch.float32 or quant_scale.numel() < 1:
+        raise ValueError("quant_scale must be a device float32 tensor with one element")
+    nv = int(quant_type) == MOE_QUANT_NVFP4
+    if quant_out is None:
+        raise ValueError("quant_out is required")
+    if quant_out.element_size() != 1:
+        raise ValueError(f"quant_out must be a byte tensor, got {quant_out.dtype}")
+    _need_bytes(quant_out, "quant_out", T * H // 2 if nv else T * H, exact=True)
+    if nv:
+        if scale_out is None:
+            raise ValueError("scale_out is required for NVFP4")
+        _need_bytes(scale_out, "scale_out", int(LIB.moe_finalize_sf_size(T, H, int(sf_layout))),
+                    exact=False)
 
 
 def moe_finalize_run(permuted_rows: torch.Tensor, expanded_idx_to_permuted_idx: torch.Tensor,
                      expert_scales: Optional[torch.Tensor],
                      shared_expert_output: Optional[torch.Tensor],
                      routed_scaling_factor: float, out: torch.Tensor, stream=None) -> None:
-    act, sdt, T, K = _common(permuted_rows, expanded_idx_to_permuted_idx, expert_scales)
     H = out.shape[-1]
+    act, sdt, T, K = _common(permuted_rows, expanded_idx_to_permuted_idx, expert_scales,
+                             shared_expert_output, H)
+    _need(out, "out", (T, H), permuted_rows.dtype)
     _check(LIB.moe_finalize_run(
         _ptr(permuted_rows), permuted_rows.shape[0], _ptr(expanded_idx_to_permuted_idx),
         _ptr(expert_scales), sdt, _ptr(shared_expert_output), float(routed_scaling_factor),
@@ -199,8 +265,10 @@ def moe_finalize_rmsnorm_run(permuted_rows: torch.Tensor,
                              gamma: torch.Tensor, eps: float,
                              residual_out: Optional[torch.Tensor], norm_out: torch.Tensor,
                              workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    act, sdt, T, K = _common(permuted_rows, expanded_idx_to_permuted_idx, expert_scales)
     H = residual.shape[-1]
+    act, sdt, T, K = _common(permuted_rows, expanded_idx_to_permuted_idx, expert_scales,
+                             shared_expert_output, H)
+    _rows_out(permuted_rows.dtype, T, H, residual, gamma, residual_out, norm_out)
     wp, wb = _ws(workspace)
     _check(LIB.moe_finalize_rmsnorm_run(
         _ptr(permuted_rows), permuted_rows.shape[0], _ptr(expanded_idx_to_permuted_idx),
@@ -218,8 +286,12 @@ def moe_finalize_quant_run(permuted_rows: torch.Tensor, expanded_idx_to_permuted
                            scale_out: Optional[torch.Tensor], sf_layout: int,
                            residual_out: Optional[torch.Tensor], norm_out: Optional[torch.Tensor],
                            workspace: Optional[torch.Tensor] = None, stream=None) -> None:
-    act, sdt, T, K = _common(permuted_rows, expanded_idx_to_permuted_idx, expert_scales)
     H = residual.shape[-1]
+    act, sdt, T, K = _common(permuted_rows, expanded_idx_to_permuted_idx, expert_scales,
+                             shared_expert_output, H)
+    _rows_out(permuted_rows.dtype, T, H, residual, gamma, residual_out, norm_out,
+              norm_optional=True)
+    _quant_out(T, H, quant_type, quant_scale, quant_out, scale_out, sf_layout)
     wp, wb = _ws(workspace)
     _check(LIB.moe_finalize_quant_run(
         _ptr(permuted_rows), permuted_rows.shape[0], _ptr(expanded_idx_to_permuted_idx),
@@ -232,9 +304,11 @@ def moe_finalize_quant_run(permuted_rows: torch.Tensor, expanded_idx_to_permuted
 def moe_quantize_run(x: torch.Tensor, quant_type: int, quant_scale: torch.Tensor,
                      quant_out: torch.Tensor, scale_out: Optional[torch.Tensor], sf_layout: int,
                      stream=None) -> None:
-    if x.dtype not in _ACT:
-        raise ValueError(f"activation dtype {x.dtype} is not bf16/fp16")
+    _act_dtype(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [T, H]")
     T, H = x.shape
+    _quant_out(T, H, quant_type, quant_scale, quant_out, scale_out, sf_layout)
     _check(LIB.moe_quantize_run(_ptr(x), T, H, _ACT[x.dtype], int(quant_type), _ptr(quant_scale),
                                 _ptr(quant_out), _ptr(scale_out), int(sf_layout),
                                 _stream(x, stream)))
@@ -244,9 +318,11 @@ def moe_residual_rmsnorm_run(x: torch.Tensor, residual: torch.Tensor, gamma: tor
                              eps: float, residual_out: Optional[torch.Tensor],
                              norm_out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
                              stream=None) -> None:
-    if x.dtype not in _ACT:
-        raise ValueError(f"activation dtype {x.dtype} is not bf16/fp16")
+    _act_dtype(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [T, H]")
     T, H = x.shape
+    _rows_out(x.dtype, T, H, residual, gamma, residual_out, norm_out)
     wp, wb = _ws(workspace)
     _check(LIB.moe_residual_rmsnorm_run(_ptr(x), _ptr(residual), _ptr(gamma), float(eps),
                                         _ptr(residual_out), _ptr(norm_out), wp, wb, T, H,
@@ -258,9 +334,11 @@ def moe_rank_sum_rmsnorm_run(rank_partials: torch.Tensor, residual: torch.Tensor
                              norm_out: torch.Tensor, workspace: Optional[torch.Tensor] = None,
                              stream=None) -> None:
     """rank_partials: [world_size, T, H]."""
-    if rank_partials.dtype not in _ACT:
-        raise ValueError(f"activation dtype {rank_partials.dtype} is not bf16/fp16")
+    _act_dtype(rank_partials, "rank_partials")
+    if rank_partials.dim() != 3:
+        raise ValueError("rank_partials must be [world_size, T, H]")
     W, T, H = rank_partials.shape
+    _rows_out(rank_partials.dtype, T, H, residual, gamma, residual_out, norm_out)
     wp, wb = _ws(workspace)
     _check(LIB.moe_rank_sum_rmsnorm_run(_ptr(rank_partials), W, _ptr(residual), _ptr(gamma),
                                         float(eps), _ptr(residual_out), _ptr(norm_out), wp, wb, T,
@@ -274,9 +352,13 @@ def moe_rank_sum_quant_run(rank_partials: torch.Tensor, residual: torch.Tensor,
                            residual_out: Optional[torch.Tensor], norm_out: Optional[torch.Tensor],
                            workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """rank_partials: [world_size, T, H]."""
-    if rank_partials.dtype not in _ACT:
-        raise ValueError(f"activation dtype {rank_partials.dtype} is not bf16/fp16")
+    _act_dtype(rank_partials, "rank_partials")
+    if rank_partials.dim() != 3:
+        raise ValueError("rank_partials must be [world_size, T, H]")
     W, T, H = rank_partials.shape
+    _rows_out(rank_partials.dtype, T, H, residual, gamma, residual_out, norm_out,
+              norm_optional=True)
+    _quant_out(T, H, quant_type, quant_scale, quant_out, scale_out, sf_layout)
     wp, wb = _ws(workspace)
     _check(LIB.moe_rank_sum_quant_run(_ptr(rank_partials), W, _ptr(residual), _ptr(gamma),
                                       float(eps), int(quant_type), _ptr(quant_scale),

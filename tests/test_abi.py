@@ -302,3 +302,56 @@ def test_cache_policy_setting():
     finally:
         M.moe_finalize_set_cache_policy(M.MOE_FIN_CACHE_AUTO)
     assert M.moe_finalize_launch_config(*small)["nontemporal"] == 0
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks shapes and dtypes before any pointer reaches the C ABI (which sees no
+    tensor extents): a tensor smaller than the call implies would be read or written past its
+    end. CPU tensors of the right shapes get as far as the device check."""
+    import torch
+    T, H, K = 4, 64, 8
+    bf = torch.bfloat16
+    rows = torch.zeros(T * K, H, dtype=bf)
+    idx = torch.zeros(T, K, dtype=torch.int32)
+    sc = torch.zeros(T, K, dtype=torch.float32)
+    res, gam = torch.zeros(T, H, dtype=bf), torch.zeros(H, dtype=bf)
+    out = torch.zeros(T, H, dtype=bf)
+
+    def fin(**kw):
+        a = dict(rows=rows, idx=idx, sc=sc, sh=None, res=res, gam=gam, ro=None, no=out)
+        a.update(kw)
+        M.moe_finalize_rmsnorm_run(a["rows"], a["idx"], a["sc"], a["sh"], 2.5, a["res"], a["gam"],
+                                   1e-6, a["ro"], a["no"])
+
+    cases = [
+        (dict(res=torch.zeros(T - 1, H, dtype=bf)), "residual must have shape"),
+        (dict(gam=torch.zeros(H - 8, dtype=bf)), "gamma must have shape"),
+        (dict(gam=torch.zeros(H, dtype=torch.float16)), "gamma must be"),
+        (dict(idx=torch.zeros(T, K, dtype=torch.int64)), "must be torch.int32"),
+        (dict(sc=torch.zeros(T, K - 1)), "expert_scales must have shape"),
+        (dict(sc=torch.zeros(T, K, dtype=torch.float64)), "expert_scales must be"),
+        (dict(sh=torch.zeros(T, H + 8, dtype=bf)), "shared_expert_output must have shape"),
+        (dict(ro=torch.zeros(T, H, dtype=torch.float16)), "residual_out must be"),
+        (dict(no=torch.zeros(T + 1, H, dtype=bf)), "norm_out must have shape"),
+        (dict(rows=torch.zeros(T * K, H - 8, dtype=bf)), "permuted_rows must have shape"),
+        (dict(rows=torch.zeros(T * K, H, dtype=torch.float32)), "is not bf16/fp16"),
+        (dict(), "device (HIP) tensors"),            # shapes fine: stops at the device check
+    ]
+    for kw, msg in cases:
+        with pytest.raises(ValueError, match=re.escape(msg)):
+            fin(**kw)
+    qs = torch.ones(1)
+    for qo, so, msg in [(torch.zeros(T, H // 2 - 1, dtype=torch.uint8), torch.zeros(4096, dtype=torch.uint8),
+                         "quant_out must hold exactly"),
+                        (torch.zeros(T, H // 2, dtype=torch.uint8), torch.zeros(16, dtype=torch.uint8),
+                         "scale_out must hold at least"),
+                        (torch.zeros(T, H // 2, dtype=torch.uint8), None, "scale_out is required")]:
+        with pytest.raises(ValueError, match=re.escape(msg)):
+            M.moe_quantize_run(out, M.MOE_QUANT_NVFP4, qs, qo, so, M.MOE_SF_SWIZZLED_128x4)
+    with pytest.raises(ValueError, match="quant_scale"):
+        M.moe_quantize_run(out, M.MOE_QUANT_FP8_E4M3, torch.ones(1, dtype=torch.float64),
+                           torch.zeros(T, H, dtype=torch.uint8), None, 0)
+    with pytest.raises(ValueError, match=re.escape("rank_partials must be [world_size, T, H]")):
+        M.moe_rank_sum_rmsnorm_run(torch.zeros(T, H, dtype=bf), res, gam, 1e-6, None, out)
+    with pytest.raises(ValueError, match=re.escape("residual must have shape")):
+        M.moe_rank_sum_rmsnorm_run(torch.zeros(2, T, H, dtype=bf), res[:2], gam, 1e-6, None, out)
