@@ -538,9 +538,18 @@ static int next_pow2(int x) {
   return p;
 }
 
+// Route groups of the row modes (same-run A/B on MI355X over top_k 1..22, T = 1..256): the
+// fewest groups that leave each group at most 4 routes (top_k 8: 2 groups of 4 routes beat 4
+// groups of 2 by 0.15 us at decode and 0.44 us at T = 32; top_k 16 and 22: 4 groups beat 2 by
+// 0.3-0.7 us), at least two wavefronts per workgroup when the routes allow it, and halved while
+// the groups span more than 512 lanes unless a group would then carry more than 8 routes
+// (T = 64, top_k 8: one group of 5 wavefronts beats two; top_k 16 or 22 keep two).
 static void finish_config(int K, Config* c) {
   int G = 1;
-  while (G < 4 && 2 * G * c->L <= 1024 && 2 * G <= K) G *= 2;
+  while (G < 4 && 2 * G * c->L <= 1024 && 2 * G <= K &&
+         ((K + G - 1) / G > 4 || G * c->L < 128))
+    G *= 2;
+  while (G > 1 && G * c->L > 512 && (K + G / 2 - 1) / (G / 2) <= 8) G /= 2;
   c->G = G;
   const int J = (K + G - 1) / G;
   c->JMAX = next_pow2(J < 4 ? 4 : J);
@@ -569,7 +578,7 @@ static int choose_slices(int64_t T, int nv) {
 // wavefront keeps at least 4 routes in flight and the grid stays near 2048 wavefronts (measured
 // best on MI355X: G = 2 at K = 8 for small batches, G = 1 from T = 128, G = 4 at K >= 16 on
 // small grids). Row modes: one workgroup per token and slice (slices = 1 covers the whole row
-// with P slots per lane), with as many route groups as fit in 1024 lanes.
+// with P slots per lane), route groups as finish_config chooses.
 static bool make_config(int mode, int64_t T, int H, int K, int slices, Config* c) {
   const int nv = H / 8;
   c->nontemporal = false;
