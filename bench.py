@@ -231,8 +231,7 @@ def main():
         "stream_ceiling_same_bytes_us": round(ceil_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_GBS, 4), "traffic": measured_traffic(),
-                     "kernel": "mfin::finalize_kernel<0, 1, 1, 1, 8, 2> (bf16, RMSNorm, whole rows, "
-                               "nontemporal streams)",
+                     "kernel": _headline_kernel(M, T, H, K),
                      "per_launch_bytes": nbytes, "kernel_source_hash": kernel_source_hash(),
                      "stream_ceiling_GBs": round(nbytes / (ceil_us * 1e-6) / 1e9, 1),
                      "frac_of_stream_ceiling": round(ceil_us / us_per_call, 4)},
@@ -245,6 +244,15 @@ def main():
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, nbytes, a.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def _headline_kernel(M, T, H, K):
+    """Names the headline call's kernel and the launch configuration the library picks for it."""
+    c = M.moe_finalize_launch_config(1, T, H, K, True)
+    return (f"mfin::finalize_kernel<0, 1, {c['route_groups']}, {c['slots_per_lane']}, 8, "
+            f"{2 if c['nontemporal'] else 0}> (bf16, RMSNorm): {c['slices']} workgroup(s) per token "
+            f"x {c['lanes']} lanes, {c['route_groups']} route group(s)"
+            f"{', nontemporal streams' if c['nontemporal'] else ''}")
 
 
 def _copy_reference(torch, stream, dev, nbytes, n_sets, replays=20):

@@ -558,12 +558,15 @@ static void finish_config(int K, Config* c) {
 
 // Slices per token for the split row modes. A CU keeps only so many vector memory requests in
 // flight, so a whole row per workgroup leaves bandwidth unused when there are fewer tokens than
-// CUs; splitting costs one cross-workgroup exchange (~1 us). Measured on MI355X, the best count
-// gives about one workgroup per CU: min(slots / 64, 224 / T) (whole rows from T = 128 on), with
-// every slice at least one wavefront of 8-element slots wide. 1 = whole rows (no workspace).
-static int choose_slices(int64_t T, int nv) {
-  const int max_by_h = nv / 64;
-  int S = (int)(224 / (T > 0 ? T : 1));
+// CUs; splitting costs one cross-workgroup exchange (~1 us). Measured on MI355X (forced slice
+// counts, T = 1..256, hidden 1024..16384, top_k 6..22): up to top_k 8 the best slices hold at
+// least 128 slots and give at most one workgroup per CU, min(slots / 128, 256 / T) (hidden 7168:
+// 7 slices at T = 32, 4 at T = 64, 2 at T = 96..128, whole rows from T = 256); with more routes
+// per token, smaller slices of 64 slots and ~224 workgroups, min(slots / 64, 224 / T), win.
+// 1 = whole rows (no workspace).
+static int choose_slices(int64_t T, int nv, int K) {
+  const int max_by_h = nv / (K > 8 ? 64 : 128);
+  int S = (int)((K > 8 ? 224 : 256) / (T > 0 ? T : 1));
   if (S > max_by_h) S = max_by_h;
   if (S > kMaxSlices) S = kMaxSlices;
   for (; S > 1; --S) {
@@ -576,8 +579,9 @@ static int choose_slices(int64_t T, int nv) {
 
 // Finalize-only: one workgroup per token and 64-slot slice, with route groups of at most 4
 // routes each while the grid stays near 2048 wavefronts (G = 2 at K = 8 for small batches,
-// G = 1 from T = 128, G = 4 at K >= 9 on small grids). Row modes: one workgroup per token and slice (slices = 1 covers the whole row
-// with P slots per lane), route groups as finish_config chooses.
+// G = 1 from T = 128, G = 4 at K >= 9 on small grids). Row modes: one workgroup per token and
+// slice (slices = 1 covers the whole row with P slots per lane), route groups as finish_config
+// chooses.
 static bool make_config(int mode, int64_t T, int H, int K, int slices, Config* c) {
   const int nv = H / 8;
   c->nontemporal = false;
@@ -761,7 +765,7 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
                     float eps, void* residual_out, void* norm_out, const float* qscale,
                     void* quant_out, void* scale_out, int sf_layout, void* workspace,
                     void* stream, int route_stride = 0) {
-  const int slices = workspace ? choose_slices(c.T, (int)(c.H / 8)) : 1;
+  const int slices = workspace ? choose_slices(c.T, (int)(c.H / 8), c.K) : 1;
   Config cfg;
   if (!make_config(mode, c.T, (int)c.H, c.K, slices, &cfg)) return MOE_FIN_ERR_HIDDEN;
   cfg.nontemporal = use_nontemporal(c.T, c.H, c.K);
@@ -967,7 +971,7 @@ static int entry_config(int entry, int64_t num_tokens, int64_t hidden, int top_k
   if (hidden <= 0 || hidden % 8 != 0 || (entry > 0 && hidden > 16384)) return MOE_FIN_ERR_HIDDEN;
   if (num_tokens < 0 || num_tokens > INT32_MAX / 2) return MOE_FIN_ERR_BAD_SHAPE;
   const int64_t T = num_tokens > 0 ? num_tokens : 1;
-  const int slices = entry > 0 && with_workspace ? choose_slices(T, (int)(hidden / 8)) : 1;
+  const int slices = entry > 0 && with_workspace ? choose_slices(T, (int)(hidden / 8), top_k) : 1;
   if (!make_config(entry == 0 ? MODE_FIN : MODE_RMS, T, (int)hidden, top_k, slices, c))
     return MOE_FIN_ERR_HIDDEN;
   c->nontemporal = use_nontemporal(T, hidden, top_k);

@@ -240,7 +240,8 @@ def test_launch_config_every_shape_has_a_kernel():
     entry kind, with and without a workspace): the chosen configuration has a compiled kernel, fits
     one workgroup (whole wavefronts, <= 1024 lanes, <= 64 KiB LDS), gives every route group work,
     covers each token's 8-element slots with non-empty slices, splits rows only within the slice
-    rule's bounds (<= hidden/512 slices, <= 224/T, <= 64; whole rows without a workspace), and
+    rule's bounds (<= 64; up to top_k 8 <= hidden/1024 slices and <= 256/T, above it <= hidden/512
+    and <= 224/T; whole rows without a workspace), and
     streams nontemporally exactly from 4 MiB of rows."""
     Ts = [1, 2, 3, 4, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 112, 127, 128, 129, 224, 225,
           256, 1000, 2048, 4096]
@@ -273,7 +274,8 @@ def test_launch_config_every_shape_has_a_kernel():
                             continue
                         S = c["slices"]
                         assert c["workgroups"] == T * S, where
-                        assert 1 <= S <= max(1, min(nv // 64, 224 // T, 64)), where
+                        bound = min(nv // 64, 224 // T) if K > 8 else min(nv // 128, 256 // T)
+                        assert 1 <= S <= max(1, min(bound, 64)), where
                         if not ws:
                             assert S == 1, where
                         assert (S - 1) * span < nv <= S * span, where

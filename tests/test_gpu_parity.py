@@ -881,14 +881,15 @@ def test_split_row_timeout_is_flagged_and_bounded():
     gives up after the kernel's own bounded wait, sets the sticky flag in the workspace header and
     exits; the call completes. A zero-filled workspace then works again."""
     import time
-    inp = make_inputs(1, 1024, 8, seed=800)          # T=1, hidden 1024: two slices per row
+    inp = make_inputs(1, 2048, 8, seed=800)          # T=1, hidden 2048: two slices per row
+    assert M.moe_finalize_launch_config(1, 1, 2048, 8)["slices"] == 2
     d = to_dev(inp)
-    need = M.moe_finalize_workspace_size(1, 1024, 8)
+    need = M.moe_finalize_workspace_size(1, 2048, 8)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     slots = ws[256:256 + 512].view(torch.int64)
     slots[0::2] = 5 << 32                             # slice 0 will wait for epoch 6 ...
     slots[1::2] = 9 << 32                             # ... slice 1 for epoch 10
-    ro = torch.empty(1, 1024, dtype=torch.bfloat16, device="cuda")
+    ro = torch.empty(1, 2048, dtype=torch.bfloat16, device="cuda")
     no = torch.empty_like(ro)
     _say("forcing a split-row timeout (bounded wait, a few seconds)")
     t0 = time.time()
