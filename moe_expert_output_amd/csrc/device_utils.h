@@ -111,12 +111,13 @@ __device__ __forceinline__ float pair_max(float v) {
   return fmaxf(v, o);
 }
 
-// --- exact-decision narrow encoders (inputs are exact FP64 magnitudes) -------------------------
+// --- exact-decision narrow encoders ------------------------------------------------------------
 // Branch-free: every lane runs the same instruction stream, so the codes of a lane's 8 elements
 // are independent chains the compiler can interleave.
 //
-// OCP E4M3 ("fn"): bias 7, 3 mantissa bits, subnormals m * 2^-9, max 448. Round to nearest
-// even, saturate at 448. y >= 0, finite, infinite or NaN. Returns the 7-bit magnitude code.
+// OCP E4M3 ("fn") of an exact float64 magnitude y: bias 7, 3 mantissa bits, subnormals m * 2^-9,
+// max 448. Round to nearest even, saturate at 448. y >= 0, finite, infinite or NaN. Returns the
+// 7-bit magnitude code.
 __device__ __forceinline__ uint32_t e4m3_code(double y) {
   const double yc = __builtin_fmin(y, 448.0);   // saturation (a NaN y is handled at the end)
   // yc = m * 2^e with m in [1, 2); below 2^-6 (zero included) the spacing stays 2^-9
@@ -135,29 +136,30 @@ __device__ __forceinline__ double e4m3_value(uint32_t c) {
   return __builtin_amdgcn_ldexp((double)mant, sh);
 }
 
-// Sign bit of d. A difference of two doubles is zero only when they are equal (gradual
-// underflow), so the sign of x - y decides x < y exactly.
-__device__ __forceinline__ uint32_t neg_bit(double d) {
-  return (uint32_t)(__builtin_bit_cast(uint64_t, d) >> 63);
-}
-
-// E2M1 magnitude code of a*gs/sf given a_gs = |x| * gs (exact) and sf >= 0: round to nearest
-// even among {0, .5, 1, 1.5, 2, 3, 4, 6} (codes 0..7), saturate at 6; 0 for NaN. Comparing a_gs
-// against midpoint*sf (exact products of narrow values) avoids any division. Each comparison is
-// the sign of one subtraction rather than a compare into VCC, so the seven tests of a lane's
-// eight elements are independent and overlap.
-__device__ __forceinline__ uint32_t e2m1_code(double a_gs, double sf) {
-  // ties to the even code: midpoints 0.25, 1.25, 2.5, 5 go down (count a_gs > m * sf);
-  // 0.75, 1.75, 3.5 go up (count a_gs >= m * sf, i.e. 1 - [a_gs < m * sf])
-  const uint32_t above = neg_bit(0.25 * sf - a_gs) + neg_bit(1.25 * sf - a_gs) +
-                         neg_bit(2.5 * sf - a_gs) + neg_bit(5.0 * sf - a_gs);
-  const uint32_t below =
-      neg_bit(a_gs - 0.75 * sf) + neg_bit(a_gs - 1.75 * sf) + neg_bit(a_gs - 3.5 * sf);
-  return a_gs == a_gs ? above + 3u - below : 0u;
-}
-
 __device__ __forceinline__ uint32_t sign_bit(float x) {
   return __builtin_bit_cast(uint32_t, x) >> 31;
+}
+
+// E2M1 magnitude code of a*gs/sf for a = |x| (a bf16/fp16 value), the float32 global scale gs
+// and the E4M3 block scale sf > 0: round to nearest even among {0, .5, 1, 1.5, 2, 3, 4, 6}
+// (codes 0..7), saturate at 6; 0 for NaN. No division: each decision compares a*gs with
+// m*sf for a rounding midpoint m. m*sf is exact in float32 (a 3-bit by 4-bit product), and
+// fma(a, gs, -m*sf) rounds the exact difference a*gs - m*sf once, so its sign is the exact
+// sign: a nonzero difference is at least 2^-42 in magnitude (a*gs carries at most 32
+// significant bits and m*sf >= 2^-11), far above the float32 subnormals. Each test is the sign
+// bit of one FMA: no compare result goes through VCC, and the seven tests of a lane's eight
+// elements overlap.
+__device__ __forceinline__ uint32_t e2m1_code(float a, float gs, float sf) {
+  // ties to the even code: midpoints 0.25, 1.25, 2.5, 5 go down (count a*gs > m*sf);
+  // 0.75, 1.75, 3.5 go up (count a*gs >= m*sf, i.e. 1 - [a*gs < m*sf])
+  const uint32_t above = sign_bit(__builtin_fmaf(-a, gs, 0.25f * sf)) +
+                         sign_bit(__builtin_fmaf(-a, gs, 1.25f * sf)) +
+                         sign_bit(__builtin_fmaf(-a, gs, 2.5f * sf)) +
+                         sign_bit(__builtin_fmaf(-a, gs, 5.0f * sf));
+  const uint32_t below = sign_bit(__builtin_fmaf(a, gs, -0.75f * sf)) +
+                         sign_bit(__builtin_fmaf(a, gs, -1.75f * sf)) +
+                         sign_bit(__builtin_fmaf(a, gs, -3.5f * sf));
+  return a == a ? above + 3u - below : 0u;
 }
 
 }  // namespace mfin

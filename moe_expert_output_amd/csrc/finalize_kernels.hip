@@ -132,14 +132,15 @@ __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
     amax = pair_max(amax);
     const bool nan_blk = pair_max(nan_here) != 0.f;
     const uint32_t sfc = nan_blk ? 0x7Fu : e4m3_code((double)amax * qs / 6.0);
-    const double sf = e4m3_value(sfc);
+    const float sf = (float)e4m3_value(sfc);    // exact: an E4M3 value
+    const float gs = (float)qs;                 // exact: the caller's float32 scale
     // a zero block scale gives signed zero codes; a NaN block gives zero codes without signs
     const uint32_t keep = sfc != 0 && !nan_blk ? 7u : 0u;
     const uint32_t sign_keep = nan_blk ? 0u : 1u;
     uint32_t word = 0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const uint32_t m = e2m1_code(__builtin_fabs((double)nr[e]) * qs, sf) & keep;
+      const uint32_t m = e2m1_code(__builtin_fabsf(nr[e]), gs, sf) & keep;
       word |= (m | ((sign_bit(nr[e]) & sign_keep) << 3)) << (4 * e);
     }
     __builtin_amdgcn_raw_buffer_store_b32(word, q_r, voff >> 2, 0, 0);
