@@ -563,9 +563,11 @@ static void finish_config(int K, Config* c) {
 // counts, T = 1..256, hidden 1024..16384, top_k 6..22): up to top_k 8 the best slices hold at
 // least 128 slots and give at most one workgroup per CU, min(slots / 128, 256 / T) (hidden 7168:
 // 7 slices at T = 32, 4 at T = 64, 2 at T = 96..128, whole rows from T = 256); with more routes
-// per token, smaller slices of 64 slots and ~224 workgroups, min(slots / 64, 224 / T), win.
-// 1 = whole rows (no workspace).
+// per token, smaller slices of 64 slots and ~224 workgroups, min(slots / 64, 224 / T), win; with
+// four routes or fewer (about five rows of data per token, e.g. a four-rank sum) whole rows win
+// from T = 96 (0.14-0.16 us at T = 96 and 128, hidden 7168). 1 = whole rows (no workspace).
 static int choose_slices(int64_t T, int nv, int K) {
+  if (K <= 4 && T >= 96) return 1;
   const int max_by_h = nv / (K > 8 ? 64 : 128);
   int S = (int)((K > 8 ? 224 : 256) / (T > 0 ? T : 1));
   if (S > max_by_h) S = max_by_h;
