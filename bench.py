@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -35,16 +36,26 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ["moe_expert_output_amd/csrc/finalize_kernels.hip",
                   "moe_expert_output_amd/csrc/device_utils.h"]
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (two runs), scaled
-# by the same counters' reading for a plain copy of known size; valid only for the kernel
-# sources it was taken with.
+# by the same counters' reading for a plain copy of known size; valid only for the kernel code
+# it was taken with.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_finalize_rmsnorm_T128_H7168_K8.json")
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed: what the compiler sees (the
+    sources hold no string literal with a comment marker in it)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash():
+    """Hash of the kernel sources' code (comments and whitespace excluded, so editing a comment
+    keeps a traffic measurement valid)."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,8 +15,9 @@
 //             (vector-width guard, layout whitelist, null-guarded optional outputs).
 //
 // Kernel design (gfx950, wave64). One workgroup handles one token and a contiguous range of
-// 8-element (16-byte) hidden slots; for the RMSNorm modes the range is the whole row so the sum
-// of squares stays inside the workgroup. The workgroup's lanes are split into G route groups of
+// 8-element (16-byte) hidden slots. For the RMSNorm modes the range is the whole row, or, with a
+// caller's workspace, one of S slices of it whose partial sums of squares are exchanged through
+// that workspace (see "Split rows"). The workgroup's lanes are split into G route groups of
 // L lanes (L a multiple of 64, so every wavefront belongs to one group); group g takes routes
 // g, g+G, g+2G, ... Every wavefront first loads all K indices and scales of its token in one
 // coalesced load (lane k holds route k) and reads them back with readlane, so row addresses are
@@ -25,7 +26,7 @@
 // through LDS, which adds them in group order (deterministic). Group 0 applies the routed
 // scaling and shared add, rounds once, adds the residual, and reduces the sum of squares with a
 // DPP wavefront reduction plus one LDS pass across wavefronts. Quantized outputs are encoded
-// with exact rounding decisions made in float64.
+// with exact rounding decisions (E4M3 in float64, E2M1 as exact signs of float32 FMAs).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
