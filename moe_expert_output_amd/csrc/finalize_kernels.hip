@@ -384,8 +384,12 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   }
   lds_barrier();
   if (tid < 64) {                               // wavefront 0 of the workgroup
+    // lane i reads wavefront i's partial (all reads in flight together); the partials are then
+    // added in wavefront order through readlane, without waiting on LDS between the adds
+    const float part = tid < n_waves0 ? wave_part[tid] : 0.f;
     float tot = 0.f;
-    for (int i = 0; i < n_waves0; ++i) tot += wave_part[i];
+    for (int i = 0; i < n_waves0; ++i)
+      tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, part), i));
     if (a.slices > 1) {
       uint64_t* slot = (uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken);
       const int S = a.slices;
