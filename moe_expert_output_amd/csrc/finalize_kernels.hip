@@ -325,12 +325,21 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     }
     lds_barrier();
     if (g == 0) {
+      // every group's partials are read first (the reads overlap), then added in group order
+      float4 u[G - 1][P][2];
+#pragma unroll
+      for (int gg = 1; gg < G; ++gg)
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const float4* src = lds_dyn + ((size_t)((gg - 1) * P + p) * L + lane) * 2;
+          u[gg - 1][p][0] = src[0];
+          u[gg - 1][p][1] = src[1];
+        }
 #pragma unroll
       for (int gg = 1; gg < G; ++gg) {
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-          const float4* src = lds_dyn + ((size_t)((gg - 1) * P + p) * L + lane) * 2;
-          float4 u0 = src[0], u1 = src[1];
+          const float4 u0 = u[gg - 1][p][0], u1 = u[gg - 1][p][1];
           acc[p][0] += u0.x; acc[p][1] += u0.y; acc[p][2] += u0.z; acc[p][3] += u0.w;
           acc[p][4] += u1.x; acc[p][5] += u1.y; acc[p][6] += u1.z; acc[p][7] += u1.w;
         }
