@@ -137,24 +137,26 @@ _TABLES = {f.name: _code_table(f) for f in (E4M3, E2M1)}
 
 
 def encode_bits(v, fmt: Fmt) -> np.ndarray:
-    """Bit pattern of values that are already exactly representable in `fmt`."""
+    """Bit pattern of values that are already exactly representable in `fmt` (ValueError
+    otherwise). A narrow format's non-NaN codes 0, 1, 2, ... have strictly increasing values, so
+    the code of |v| is its position in that table; the sign adds the top bit. NaN encodes as the
+    E4M3 NaN S.1111.111 without a sign (E2M1 has no NaN; 0 is returned)."""
     v = np.asarray(v, dtype=np.float64)
     if fmt is BF16:
         return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     if fmt is FP16:
         return v.astype(np.float16).view(np.uint16)
     table = _TABLES[fmt.name]
+    finite = table[~np.isnan(table)]
     sign_bit = 1 << (fmt.exp_bits + fmt.frac_bits)
-    out = np.empty(v.shape, dtype=np.uint8)
-    flat_v, flat_o = v.reshape(-1), out.reshape(-1)
-    lookup = {float(val): c for c, val in enumerate(table) if not np.isnan(val)}
-    for i, val in enumerate(flat_v):
-        if np.isnan(val):
-            flat_o[i] = sign_bit - 1 if fmt is E4M3 else 0   # E2M1 has no NaN: never produced
-            continue
-        c = lookup[float(abs(val))]
-        flat_o[i] = c | (sign_bit if np.signbit(val) else 0)
-    return out
+    nan = np.isnan(v)
+    a = np.where(nan, 0.0, np.abs(v))
+    c = np.minimum(np.searchsorted(finite, a), finite.size - 1)
+    if not np.array_equal(finite[c], a):
+        raise ValueError(f"value not representable in {fmt.name}")
+    out = c | np.where(np.signbit(v), sign_bit, 0)
+    out = np.where(nan, sign_bit - 1 if fmt is E4M3 else 0, out)
+    return out.astype(np.uint8)
 
 
 def decode_bits(bits, fmt: Fmt) -> np.ndarray:
@@ -368,19 +370,17 @@ def quant_nvfp4(N, gs: float, layout: int = SF_SWIZZLED_128x4):
         raise ValueError("H must be a multiple of 16 for NVFP4")
     gs = float(np.float32(gs))
     nb = H // NVFP4_BLOCK
-    codes4 = np.zeros((T, H), dtype=np.uint8)
+    blocks = N.reshape(T, nb, NVFP4_BLOCK)
+    amax = np.max(np.abs(blocks), axis=-1)                     # [T, nb]; NaN if the block has one
+    sf = round_to_format(gs * amax / 6.0, E4M3)
+    t_i, b_i = np.meshgrid(np.arange(T), np.arange(nb), indexing="ij")
     sf_bytes = np.zeros(sf_size(T, H, layout), dtype=np.uint8)
-    for t in range(T):
-        for b in range(nb):
-            blk = N[t, b * NVFP4_BLOCK:(b + 1) * NVFP4_BLOCK]
-            amax = float(np.max(np.abs(blk)))
-            sf = float(round_to_format(gs * amax / 6.0, E4M3))
-            sf_bytes[sf_offset(t, b, H, layout)] = encode_bits(sf, E4M3)
-            if sf == 0.0:
-                q = np.copysign(np.zeros(NVFP4_BLOCK), blk)
-            else:
-                q = round_to_format(blk * gs / sf, E2M1)
-            codes4[t, b * NVFP4_BLOCK:(b + 1) * NVFP4_BLOCK] = encode_bits(q, E2M1)
+    sf_bytes[sf_offset(t_i, b_i, H, layout)] = encode_bits(sf, E4M3)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = round_to_format(blocks * gs / sf[..., None], E2M1)
+    # a zero block scale gives signed zero codes
+    q = np.where((sf == 0.0)[..., None], np.copysign(np.zeros_like(blocks), blocks), q)
+    codes4 = encode_bits(q, E2M1).reshape(T, H)
     packed = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8)
     return packed, sf_bytes
 
