@@ -627,9 +627,23 @@ static bool make_config(int mode, int64_t T, int H, int K, int slices, Config* c
   } else {
     c->P = nv <= 1024 ? 1 : (nv <= 2048 ? 2 : 0);
     if (c->P == 0) return false;
+    c->grid_x = 1;
+    // From 1024 tokens, whole-row workgroups are rounded up to a multiple of four wavefronts
+    // (one per SIMD; the extra lanes hold no slot). Measured on MI355X, cold, bit-identical
+    // outputs: hidden 7168 top_k 8 T = 1024 / 2048 / 4096 -1.6 / -1.1 / -0.7 us, top_k 4
+    // -1.4 us, hidden 3584 top_k 16 -1.8 us, hidden 5120 top_k 8 -0.9 / -1.2 us; neutral at
+    // T = 256..768 and slower at T = 128..256 with top_k 4 (+0.15 us), where each CU holds one
+    // workgroup and the idle wavefronts' predicated loads still occupy the address units. For
+    // the same reason it is skipped when a route group carries more than 8 routes (more
+    // registers, one workgroup per CU: hidden 7168 top_k 16 was 0.7 us slower).
+    if (T >= 1024) {
+      c->L = ((nv + c->P - 1) / c->P + 255) / 256 * 256;
+      c->span = c->L * c->P;
+      finish_config(K, c);
+      if (c->JMAX <= 8) return true;
+    }
     c->L = ((nv + c->P - 1) / c->P + 63) / 64 * 64;
     c->span = c->L * c->P;
-    c->grid_x = 1;
   }
   finish_config(K, c);
   return true;

@@ -241,8 +241,9 @@ def test_launch_config_every_shape_has_a_kernel():
     one workgroup (whole wavefronts, <= 1024 lanes, <= 64 KiB LDS), gives every route group work,
     covers each token's 8-element slots with non-empty slices, splits rows only within the slice
     rule's bounds (<= 64; up to top_k 8 <= hidden/1024 slices and <= 256/T, above it <= hidden/512
-    and <= 224/T; whole rows for top_k <= 4 from T = 96 and without a workspace), and
-    streams nontemporally exactly from 4 MiB of rows."""
+    and <= 224/T; whole rows for top_k <= 4 from T = 96 and without a workspace), sizes whole-row
+    workgroups by the slot rule (four-wavefront multiples from T = 1024 while a route group has at
+    most 8 routes), and streams nontemporally exactly from 4 MiB of rows."""
     Ts = [1, 2, 3, 4, 7, 8, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 112, 127, 128, 129, 224, 225,
           256, 1000, 2048, 4096]
     Hs = [8, 16, 48, 512, 520, 1000, 1024, 1032, 2048, 3584, 4096, 4104, 6144, 7168, 8192, 8200,
@@ -282,6 +283,16 @@ def test_launch_config_every_shape_has_a_kernel():
                             assert S == 1, where
                         assert (S - 1) * span < nv <= S * span, where
                         assert S == 1 or span % 8 == 0, where
+                        if S == 1:
+                            # whole rows: one or two slots per lane, lanes rounded up to whole
+                            # wavefronts, or from 1024 tokens to four wavefronts while a route
+                            # group carries at most 8 routes
+                            assert P == (1 if nv <= 1024 else 2), where
+                            per_lane = -(-nv // P)
+                            quad = T >= 1024 and -(-K // G) <= 8
+                            r = 256 if quad else 64
+                            assert lanes_per_group == -(-per_lane // r) * r, where
+                            assert span == lanes_per_group * P, where
     assert n == 3 * 2 * len(Ts) * len(Hs) * len(Ks)
 
 

@@ -390,7 +390,7 @@ def run_quant(inp, qtype, qscale, layout=M.MOE_SF_SWIZZLED_128x4, with_norm=True
 
 
 @pytest.mark.parametrize("layout", [1, 0])
-@pytest.mark.parametrize("TH", [(64, 6144), (5, 1024), (130, 2048), (1, 48)])
+@pytest.mark.parametrize("TH", [(64, 6144), (5, 1024), (130, 2048), (1, 48), (1030, 7168)])
 def test_nvfp4(TH, layout):
     T, H = TH
     inp = make_inputs(T, H, 8, seed=workload_seed("quant", T) + H)
@@ -409,13 +409,20 @@ def test_nvfp4(TH, layout):
         c_g = qo.reshape(T, nb, 8)
         c_o = codes_or.reshape(T, nb, 8)
         sf_g, sf_o = so[offs], sf_or[offs]
-        # blocks whose norm_out equals the oracle's: codes and scales bit-exact
+        # codes and scales (padding included) are the NVFP4 quantization of the kernel's own
+        # rounded norm_out, bit for bit
+        own_c, own_s = O.quant_nvfp4(N, gs, layout)
+        assert np.array_equal(qo, own_c) and np.array_equal(so, own_s)
+        # blocks whose norm_out equals the primary oracle's: codes and scales bit-exact
         assert np.array_equal(c_g[same_blk], c_o[same_blk])
         assert np.array_equal(sf_g[same_blk], sf_o[same_blk])
         assert same_blk.mean() > 0.98, same_blk.mean()
-        # other blocks (a 1-ulp norm_out difference): scale within one E4M3 step, codes within one
+        # blocks within one ulp of it: scale within one E4M3 step
+        near_blk = ~same_blk & (ulp_distance(O.encode_bits(N, O.FORMATS["bf16"]),
+                                             O.encode_bits(ref.N, O.FORMATS["bf16"]))
+                                <= 1).reshape(T, nb, 16).all(-1)
         diff_sf = np.abs(sf_g.astype(int) - sf_o.astype(int))
-        assert diff_sf[~same_blk].max(initial=0) <= 1
+        assert diff_sf[near_blk].max(initial=0) <= 1
         # every byte outside the valid (t, b) scale positions is zero padding
         if layout == 1:
             pad = np.ones(so.size, bool)
@@ -429,9 +436,9 @@ def test_nvfp4(TH, layout):
     assert np.array_equal(qo2, qo) and np.array_equal(so2, so)
 
 
-@pytest.mark.parametrize("T", [64, 3])
-def test_fp8(T):
-    inp = make_inputs(T, 6144, 8, seed=workload_seed("quant", T) + 7)
+@pytest.mark.parametrize("T,H", [(64, 6144), (3, 6144), (1030, 5120)])
+def test_fp8(T, H):
+    inp = make_inputs(T, H, 8, seed=workload_seed("quant", T) + 7)
     ref = oracle_ref(inp)
     s8 = O.fp8_scale(ref.N)
     codes_or = O.quant_fp8(ref.N, s8)
@@ -439,10 +446,15 @@ def test_fp8(T):
         ro, no, qo, _ = run_quant(inp, M.MOE_QUANT_FP8_E4M3, s8, use_ws=use_ws)
         R, N = np64(ro), np64(no)
         check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")
+        # the codes are the FP8 quantization of the kernel's own rounded norm_out, bit for bit
+        assert np.array_equal(qo, O.quant_fp8(N, s8))
         same = N == ref.N
         assert np.array_equal(qo[same], codes_or[same])
-        # elsewhere the code moves by at most one E4M3 step in the direction of the norm change
-        d = np.abs((qo[~same] & 0x7F).astype(int) - (codes_or[~same] & 0x7F).astype(int))
+        # where norm_out is one ulp from the primary oracle's, the code moves by at most one E4M3
+        # step (farther only near cancellation, where residual_out may sit several ulps away)
+        near = ~same & (ulp_distance(O.encode_bits(N, O.FORMATS["bf16"]),
+                                     O.encode_bits(ref.N, O.FORMATS["bf16"])) <= 1)
+        d = np.abs((qo[near] & 0x7F).astype(int) - (codes_or[near] & 0x7F).astype(int))
         assert d.max(initial=0) <= 1
         assert same.mean() > 0.99
 
@@ -641,8 +653,12 @@ def test_quantize_nonfinite_bit_exact(act):
 
 
 # ---- large batches (prefill-sized calls: whole rows, nontemporal streaming) ---------------------
-@pytest.mark.parametrize("THK", [(256, 7168, 8), (512, 7168, 8), (2048, 2048, 8), (300, 3584, 16)])
+@pytest.mark.parametrize("THK", [(256, 7168, 8), (512, 7168, 8), (2048, 2048, 8), (300, 3584, 16),
+                                 (1024, 7168, 8), (1030, 5120, 8), (1024, 3584, 16),
+                                 (1024, 7168, 4), (1024, 7168, 16)])
 def test_large_batch(THK):
+    """From 1024 tokens whole-row workgroups are rounded up to four wavefronts (hidden 7168: 1024
+    lanes for 896 slots; 5120: 768 for 640), so their last lanes hold no slot."""
     T, H, K = THK
     full_check(make_inputs(T, H, K, seed=5000 + T + K))
 
