@@ -683,7 +683,7 @@ def _norm_within_1ulp(got_N, want_N, act):
 
 @pytest.mark.parametrize("act", ["bf16", "fp16"])
 @pytest.mark.parametrize("TH", [(1, 6144), (4, 1024), (37, 1032), (128, 7168), (300, 3584),
-                                (2, 16384), (5, 8)])
+                                (2, 16384), (5, 8), (1030, 7168)])
 def test_residual_rmsnorm(TH, act):
     """r = RNE(x + residual) exactly (one float32 add of two activation values, rounded once,
     equals the single rounding of the exact sum); norm within 1 ulp of the oracle's."""
@@ -939,7 +939,8 @@ def _rank_sum_inputs(T, H, W, act, seed):
 
 @pytest.mark.parametrize("act", ["bf16", "fp16"])
 @pytest.mark.parametrize("TWH", [(1, 4, 6144), (16, 4, 6144), (64, 4, 7168), (128, 4, 7168),
-                                 (128, 8, 7168), (5, 2, 1032), (3, 1, 48), (300, 8, 2048)])
+                                 (128, 8, 7168), (5, 2, 1032), (3, 1, 48), (300, 8, 2048),
+                                 (1030, 4, 5120)])
 def test_rank_sum_rmsnorm(TWH, act):
     T, W, H = TWH
     inp = _rank_sum_inputs(T, H, W, act, seed=6000 + T + 10 * W)
