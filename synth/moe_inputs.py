@@ -20,7 +20,9 @@ What is drawn, and why (no finalize arithmetic lives here):
   * shared-expert output and residual [T, H] ~ N(0,1) (times their scales); gamma = 1 + 0.1*N(0,1).
 
 Random numbers come from numpy's PCG64 generator seeded with an explicit integer, so the same
-seed gives the same inputs on every machine.
+seed gives the same inputs on every machine. Problems too large to draw on the host (gigabytes of
+rows) come from make_inputs_on_device: the same distributions from torch's seeded generator on
+the device.
 """
 from __future__ import annotations
 
@@ -121,3 +123,36 @@ def make_inputs(T: int, H: int, K: int, *, seed: int, act_dtype: str = "bf16",
                      seed=seed, rows=rows, idx=idx, scales=scales, shared=shared,
                      residual=residual, gamma=gamma, rsf=float(rsf), eps=float(eps),
                      meta={"mask_frac": mask_frac, "n_masked": n_masked})
+
+
+def make_inputs_on_device(T: int, H: int, K: int, *, seed: int, device, act_dtype: str = "bf16",
+                          mask_frac: float = 0.25, rsf: float = 2.5,
+                          eps: float = 1e-6) -> MoeInputs:
+    """The distributions of make_inputs (fp32 scales, shared expert present, n_rows = T*K), drawn
+    on `device` by torch's generator seeded with `seed`, for problems too large to draw on the
+    host. The tensors stay on `device`; the draws differ from make_inputs' for the same seed."""
+    if act_dtype not in ACT_DTYPES:
+        raise ValueError(f"act_dtype {act_dtype!r}")
+    dt = ACT_DTYPES[act_dtype]
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    n_rows = T * K
+    rows = torch.empty(n_rows, H, dtype=dt, device=device)
+    chunk = max(1, (1 << 27) // H)                 # 512 MB of float32 draws at a time
+    for r0 in range(0, n_rows, chunk):
+        r1 = min(n_rows, r0 + chunk)
+        rows[r0:r1] = torch.randn(r1 - r0, H, generator=g, device=device).to(dt)
+    perm = torch.randperm(n_rows, generator=g, device=device)
+    n_masked = int(np.floor(mask_frac * T * K))
+    if n_masked:
+        perm[torch.randperm(T * K, generator=g, device=device)[:n_masked]] = -1
+    idx = perm.reshape(T, K).to(torch.int32)
+    logits = torch.randn(T, K, generator=g, device=device, dtype=torch.float64)
+    scales = torch.softmax(logits, dim=1).to(torch.float32)
+    shared = torch.randn(T, H, generator=g, device=device).to(dt)
+    residual = torch.randn(T, H, generator=g, device=device).to(dt)
+    gamma = (1.0 + 0.1 * torch.randn(H, generator=g, device=device)).to(dt)
+    return MoeInputs(T=T, H=H, K=K, n_rows=n_rows, act_dtype=act_dtype, scale_dtype="fp32",
+                     seed=seed, rows=rows, idx=idx, scales=scales, shared=shared,
+                     residual=residual, gamma=gamma, rsf=float(rsf), eps=float(eps),
+                     meta={"mask_frac": mask_frac, "n_masked": n_masked, "device": str(device)})

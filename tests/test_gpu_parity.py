@@ -19,7 +19,7 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU containers
 
 import moe_expert_output_amd as M  # noqa: E402
 import oracle as O  # noqa: E402
-from synth import make_inputs, workload_seed  # noqa: E402
+from synth import MoeInputs, make_inputs, make_inputs_on_device, workload_seed  # noqa: E402
 from tests.comparators import ulp_distance  # noqa: E402
 from tests.parity import (bits16, check_finalize, check_norm, check_residual,  # noqa: E402
                           np64, oracle_ref, to_dev)
@@ -661,6 +661,43 @@ def test_large_batch(THK):
     lanes for 896 slots; 5120: 768 for 640), so their last lanes hold no slot."""
     T, H, K = THK
     full_check(make_inputs(T, H, K, seed=5000 + T + K))
+
+
+def test_rows_beyond_4gib_sampled_tokens():
+    """Maximum-size addressing: 17000 tokens at hidden 16384 and top_k 8 give 4.46 GB of permuted
+    rows, so routes reach rows past the 4 GiB mark. The whole batch runs through the finalize and
+    the RMSNorm entry points; the oracle checks a seeded sample of tokens plus tokens routed to
+    rows beyond 4 GiB (tokens are independent, so a sub-batch of the oracle is exact)."""
+    T, H, K = 17000, 16384, 8
+    inp = make_inputs_on_device(T, H, K, seed=7000 + T, device="cuda")
+    _say(f"case rows beyond 4 GiB: T={T} H={H} K={K} seed={inp.seed} "
+         f"rows {inp.rows.numel() * 2 / 1e9:.2f} GB")
+    assert inp.rows.numel() * 2 > (1 << 32)
+    d = to_dev(inp)
+    s = run_finalize(inp, d)
+    ro, no = run_rmsnorm(inp, d, use_ws=True)
+    idx = inp.idx.cpu().numpy()
+    far_row = (1 << 32) // (2 * H)
+    far = np.flatnonzero((idx >= far_row).any(axis=1))
+    rng = np.random.default_rng(inp.seed)
+    pick = np.unique(np.concatenate([rng.choice(T, 48, replace=False), far[:16], [0, T - 1]]))
+    assert (idx[pick] >= far_row).any()
+    sub_idx = idx[pick]
+    used = np.unique(sub_idx[sub_idx >= 0])
+    remap = np.where(sub_idx >= 0, np.searchsorted(used, np.maximum(sub_idx, 0)), -1)
+    rows_used = torch.as_tensor(used, device="cuda")
+    sub = MoeInputs(T=len(pick), H=H, K=K, n_rows=len(used), act_dtype="bf16", scale_dtype="fp32",
+                    seed=inp.seed, rows=inp.rows[rows_used].cpu(),
+                    idx=torch.from_numpy(remap.astype(np.int32)),
+                    scales=inp.scales.cpu()[pick], shared=inp.shared.cpu()[pick],
+                    residual=inp.residual.cpu()[pick], gamma=inp.gamma.cpu(), rsf=inp.rsf,
+                    eps=inp.eps)
+    ref = oracle_ref(sub)
+    sel = torch.as_tensor(pick, device="cuda")
+    _say("  ", check_finalize(np64(s[sel]), ref, "bf16"))
+    R, N = np64(ro[sel]), np64(no[sel])
+    _say("  ", check_residual(R, ref, np64(sub.residual), "bf16"))
+    _say("  ", check_norm(N, R, ref, np64(sub.gamma), inp.eps, "bf16"))
 
 
 # ---- residual + RMSNorm of a given activation (moe_residual_rmsnorm_run) -------------------------
