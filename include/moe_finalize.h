@@ -54,6 +54,10 @@
  *     same time (different streams) must use different workspaces. Its first 32-bit word is a
  *     sticky flag that a kernel sets to nonzero if a workgroup gave up waiting for the other
  *     slices of its row (outputs of that call are then unreliable); it stays 0 in normal use.
+ *     Progress: a token's slices are consecutive workgroups and rows are split only while the
+ *     grid stays near one workgroup per CU, so workgroups dispatched before a waiting one never
+ *     wait on it and the slices of a row run together. The wait is bounded (about a second)
+ *     even if other work were to hold every CU; the flag then reports it.
  */
 #ifndef MOE_FINALIZE_H_
 #define MOE_FINALIZE_H_
