@@ -127,7 +127,7 @@ def _parse():
 def main():
     a = _parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the finalize path runs on one GPU; --gpus must be 1",
                           "n_gpus": a.gpus}), flush=True)
         sys.exit(2)
 
