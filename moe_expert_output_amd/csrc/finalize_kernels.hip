@@ -170,19 +170,23 @@ __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
   }
 }
 
-// Zero the swizzled scale rows between T and the next multiple of 128: row t's workgroup takes
-// rows T + t, T + t + T, ...; its `nthreads` threads split each row's 32-bit words.
-__device__ __forceinline__ void zero_sf_padding(const QuantDst& d, int T, int t, int tid,
-                                                int nthreads) {
-  const int nb4 = ((d.H >> 4) + 3) & ~3;
-  const int words = nb4 >> 2;
-  const int t_pad_end = (T + 127) & ~127;
-  for (int rr = T + t; rr < t_pad_end; rr += T) {
-    for (int i = tid; i < words; i += nthreads) {
-      const int64_t off =
-          ((int64_t)(rr >> 7) * words + i) * 512 + (rr & 31) * 16 + ((rr & 127) >> 5) * 4;
-      *(uint32_t*)(d.sf_out + off) = 0u;
-    }
+// Zero the swizzled scale bytes of the padding rows (T up to the next multiple of 128). Only the
+// last 128-row tile has padding rows. Row r's word of a 512-byte tile sits at byte
+// (r % 32) * 16 + (r / 32) * 4, so word w of a tile belongs to row (w / 4) + 32 * (w % 4). The
+// tile's words are split over every thread of the grid (`thread` of `n_threads`) in grid-stride
+// order, so each wavefront store covers consecutive words; the words of rows below T hold
+// other workgroups' scales and are skipped.
+__device__ __forceinline__ void zero_sf_padding(const QuantDst& d, int T, int64_t thread,
+                                                int64_t n_threads) {
+  const int rem = T & 127;
+  if (rem == 0) return;
+  const int tiles = (((d.H >> 4) + 3) & ~3) >> 2;
+  uint8_t* const last = d.sf_out + (int64_t)(T >> 7) * tiles * 512;
+  const int n_words = tiles * 128;
+  for (int64_t w = thread; w < n_words; w += n_threads) {
+    const int within = (int)(w & 127);
+    const int row = (within >> 2) + 32 * (within & 3);
+    if (row >= rem) *(uint32_t*)(last + (int64_t)(w >> 7) * 512 + within * 4) = 0u;
   }
 }
 
@@ -433,7 +437,16 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     if (tid == 0) row_total = tot;
   }
   lds_barrier();
-  if (g != 0) return;
+  // the padding rows of the swizzled scale layout: every thread of the grid zeroes its share,
+  // route groups other than 0 now (they are done), group 0 after its stores
+  [[maybe_unused]] const int64_t grid_thread = (int64_t)blockIdx.x * blockDim.x + tid;
+  [[maybe_unused]] const int64_t grid_threads = (int64_t)gridDim.x * blockDim.x;
+  if (g != 0) {
+    if constexpr (MODE == MODE_NVFP4) {
+      if (a.sf_swizzled) zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T, grid_thread, grid_threads);
+    }
+    return;
+  }
   const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(row_total, a.inv_h, a.eps));
 
   const auto no_r = rsrc(a.out + tok_off, a.out ? row_bytes : 0u);
@@ -456,7 +469,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     }
   }
   if constexpr (MODE == MODE_NVFP4) {
-    if (a.sf_swizzled && slice == 0) zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T, t, tid, L);
+    if (a.sf_swizzled) zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T, grid_thread, grid_threads);
   }
 }
 
@@ -488,7 +501,8 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantParams a) {
   const QuantDst d{a.sf_out, a.H, a.sf_swizzled};
   quantize_store<MODE>(xr, qs, rsrc(a.quant_out + (int64_t)t * qrow, qrow), voff, live, s, t, d);
   if constexpr (MODE == MODE_NVFP4) {
-    if (a.sf_swizzled && slice == 0) zero_sf_padding(d, a.T, t, lane, 64);
+    if (a.sf_swizzled)
+      zero_sf_padding(d, a.T, (int64_t)blockIdx.x * 64 + lane, (int64_t)gridDim.x * 64);
   }
 }
 
