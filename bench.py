@@ -331,6 +331,8 @@ def _sweep_cases(large):
     c += [("highk", e, t, h, k, "bf16", sdt, False, None)
           for (h, k) in ((2048, 22), (3584, 16), (2048, 6), (2048, 10))
           for sdt in ("fp32", "bf16") for t in (1, 8, 16, 32) for e in ("finalize", "rmsnorm")]
+    c += [("quant", "quant", t, 6144, 8, "bf16", "fp32", True, q)
+          for t in (1, 16) for q in ("nvfp4", "nvfp4_linear", "fp8")]
     c += [("quant", "quant", 64, 6144, 8, "bf16", "fp32", True, q)
           for q in ("nvfp4", "nvfp4+norm", "nvfp4_linear", "fp8", "fp8+norm")]
     c += [("quant", "quant_two_kernel", 64, 6144, 8, "bf16", "fp32", True, q)

@@ -435,18 +435,19 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
         tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)bits, j));
     }
     if (tid == 0) row_total = tot;
+  } else {
+    // The padding rows of the swizzled scale layout are zeroed by the wavefronts that would
+    // otherwise only wait here while wavefront 0 sums the row (and, for split rows, waits for the
+    // other slices): every thread past the first wavefront of every workgroup takes a share.
+    if constexpr (MODE == MODE_NVFP4) {
+      if (a.sf_swizzled)
+        zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T,
+                        (int64_t)blockIdx.x * (blockDim.x - 64) + (tid - 64),
+                        (int64_t)gridDim.x * (blockDim.x - 64));
+    }
   }
   lds_barrier();
-  // the padding rows of the swizzled scale layout: every thread of the grid zeroes its share,
-  // route groups other than 0 now (they are done), group 0 after its stores
-  [[maybe_unused]] const int64_t grid_thread = (int64_t)blockIdx.x * blockDim.x + tid;
-  [[maybe_unused]] const int64_t grid_threads = (int64_t)gridDim.x * blockDim.x;
-  if (g != 0) {
-    if constexpr (MODE == MODE_NVFP4) {
-      if (a.sf_swizzled) zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T, grid_thread, grid_threads);
-    }
-    return;
-  }
+  if (g != 0) return;
   const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(row_total, a.inv_h, a.eps));
 
   const auto no_r = rsrc(a.out + tok_off, a.out ? row_bytes : 0u);
@@ -469,7 +470,11 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     }
   }
   if constexpr (MODE == MODE_NVFP4) {
-    if (a.sf_swizzled) zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T, grid_thread, grid_threads);
+    // workgroups of a single wavefront have nobody waiting above: the wavefront zeroes the
+    // padding rows itself, after its stores
+    if (a.sf_swizzled && blockDim.x == 64)
+      zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T, (int64_t)blockIdx.x * 64 + tid,
+                      (int64_t)gridDim.x * 64);
   }
 }
 
