@@ -486,10 +486,21 @@ struct QuantParams {
   uint8_t* quant_out;
   uint8_t* sf_out;
   int T, H, nv, slices, sf_swizzled;
+  int pad_blocks;   // workgroups after the T * slices quantizing ones that only zero scale padding
 };
 
 template <int ACT, int MODE>
 __global__ __launch_bounds__(64) void quantize_kernel(const QuantParams a) {
+  if constexpr (MODE == MODE_NVFP4) {
+    // the swizzled layout's padding rows are zeroed by workgroups of their own, in parallel
+    // with the quantizing ones (one workgroup per token and slice is too few at decode sizes)
+    const int64_t n_main = (int64_t)a.T * a.slices;
+    if (blockIdx.x >= n_main) {
+      zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T, (blockIdx.x - n_main) * 64 + threadIdx.x,
+                      (int64_t)a.pad_blocks * 64);
+      return;
+    }
+  }
   const int t = blockIdx.x / a.slices;
   const int slice = blockIdx.x - t * a.slices;
   const int lane = threadIdx.x;
@@ -505,10 +516,6 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantParams a) {
   const uint32_t qrow = MODE == MODE_FP8 ? (uint32_t)a.H : (uint32_t)a.H / 2u;
   const QuantDst d{a.sf_out, a.H, a.sf_swizzled};
   quantize_store<MODE>(xr, qs, rsrc(a.quant_out + (int64_t)t * qrow, qrow), voff, live, s, t, d);
-  if constexpr (MODE == MODE_NVFP4) {
-    if (a.sf_swizzled)
-      zero_sf_padding(d, a.T, (int64_t)blockIdx.x * 64 + lane, (int64_t)gridDim.x * 64);
-  }
 }
 
 // An empty kernel launched with a finalize entry point's grid, block and LDS: its duration is the
@@ -1197,8 +1204,12 @@ int moe_quantize_run(const void* x, int64_t num_tokens, int64_t hidden, int act_
   p.nv = (int)(hidden / 8);
   p.slices = (p.nv + 63) / 64;
   p.sf_swizzled = sf_layout == MOE_SF_SWIZZLED_128x4;
-  if ((int64_t)p.slices * num_tokens > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
-  const dim3 grid((unsigned)(p.slices * num_tokens)), block(64);
+  // padding rows (swizzled NVFP4, T not a multiple of 128): about two words per thread
+  p.pad_blocks = nvfp4 && p.sf_swizzled && (num_tokens % 128) != 0
+                     ? (int)((((hidden / 16 + 3) / 4) * 128 + 127) / 128)
+                     : 0;
+  if ((int64_t)p.slices * num_tokens + p.pad_blocks > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
+  const dim3 grid((unsigned)(p.slices * num_tokens + p.pad_blocks)), block(64);
   hipStream_t s = (hipStream_t)stream;
   if (act_dtype == MOE_DTYPE_BF16) {
     if (nvfp4) hipLaunchKernelGGL((quantize_kernel<ACT_BF16, MODE_NVFP4>), grid, block, 0, s, p);
