@@ -56,7 +56,8 @@
  *     slices of its row (outputs of that call are then unreliable); it stays 0 in normal use.
  *     Progress: a token's slices are consecutive workgroups and rows are split only while the
  *     grid stays near one workgroup per CU, so workgroups dispatched before a waiting one never
- *     wait on it and the slices of a row run together. The wait is bounded (about a second)
+ *     wait on it (the scale-padding workgroups of an NVFP4 call come last and wait on nothing)
+ *     and the slices of a row run together. The wait is bounded (about a second)
  *     even if other work were to hold every CU; the flag then reports it.
  */
 #ifndef MOE_FINALIZE_H_
@@ -277,7 +278,9 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
  * moe_finalize_run, 1 = moe_finalize_rmsnorm_run, 2 = moe_finalize_quant_run) chooses for a shape,
  * with (with_workspace != 0) or without a workspace. Host-only, never touches the GPU. Writes
  * MOE_FIN_LAUNCH_CONFIG_FIELDS int64 values to `out` (n_out is the caller's array length):
- *   out[0] workgroups in the grid (0 when num_tokens == 0)
+ *   out[0] workgroups in the grid (0 when num_tokens == 0); a swizzled NVFP4 call whose
+ *          num_tokens is not a multiple of 128 adds a few workgroups after these that only
+ *          zero the scale bytes of the padding rows
  *   out[1] lanes per workgroup (route groups x lanes per group, a multiple of 64, <= 1024)
  *   out[2] workgroups per token for the RMSNorm entries (slices of a split row; 1 = whole rows)
  *   out[3] route groups G (wavefront groups that split top_k; partials combined in LDS)

@@ -66,6 +66,8 @@ struct Params {
   int slices;                // workgroups per token (> 1: the row is split, see below)
   uint8_t* ws;               // workspace of the split row modes (null when slices == 1)
   int route_stride;          // > 0: no route map; route k of token t is row k * route_stride + t
+  int pad_blocks;            // NVFP4, swizzled scales: workgroups after the token ones that
+                             // only zero the scale bytes of the padding rows
 };
 
 // Split rows. When a token's row is spread over `slices` workgroups, each workgroup publishes
@@ -195,9 +197,23 @@ __device__ __forceinline__ void zero_sf_padding(const QuantDst& d, int T, int64_
 // cacheable. NT = 0 leaves them all cacheable.
 template <int ACT, int MODE, int G, int P, int JMAX, int NT>
 __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
-  // blockIdx.x = token * slices + slice (one slice per token in the whole-row modes)
-  const int t = blockIdx.x / a.slices;
-  const int slice = blockIdx.x - t * a.slices;
+  // blockIdx.x = token * slices + slice (one slice per token in the whole-row modes). For NVFP4
+  // with swizzled scales, pad_blocks workgroups after those only zero the scale bytes of the
+  // padding rows (same-box A/B: after the token workgroups beat before them by up to 0.2 us at
+  // T = 64, and beat zeroing in the token workgroups, which cost 1 us at T = 1 when few of
+  // their wavefronts are idle). They wait on nothing, so no split row's exchange waits on them.
+  const int bid = blockIdx.x;
+  if constexpr (MODE == MODE_NVFP4) {
+    const int n_main = a.T * a.slices;
+    if (bid >= n_main) {
+      zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T,
+                      (int64_t)(bid - n_main) * blockDim.x + threadIdx.x,
+                      (int64_t)a.pad_blocks * blockDim.x);
+      return;
+    }
+  }
+  const int t = bid / a.slices;
+  const int slice = bid - t * a.slices;
   const int tid = threadIdx.x;
   const int L = a.lanes;
   const int g = __builtin_amdgcn_readfirstlane(tid / L);   // wave-uniform route group
@@ -435,16 +451,6 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
         tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)bits, j));
     }
     if (tid == 0) row_total = tot;
-  } else {
-    // The padding rows of the swizzled scale layout are zeroed by the wavefronts that would
-    // otherwise only wait here while wavefront 0 sums the row (and, for split rows, waits for the
-    // other slices): every thread past the first wavefront of every workgroup takes a share.
-    if constexpr (MODE == MODE_NVFP4) {
-      if (a.sf_swizzled)
-        zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T,
-                        (int64_t)blockIdx.x * (blockDim.x - 64) + (tid - 64),
-                        (int64_t)gridDim.x * (blockDim.x - 64));
-    }
   }
   lds_barrier();
   if (g != 0) return;
@@ -468,13 +474,6 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
       quantize_store<MODE>(nr, qs, q_r, voff[p], live[p], slot0 + lane + p * L, t,
                            QuantDst{a.sf_out, a.H, a.sf_swizzled});
     }
-  }
-  if constexpr (MODE == MODE_NVFP4) {
-    // workgroups of a single wavefront have nobody waiting above: the wavefront zeroes the
-    // padding rows itself, after its stores
-    if (a.sf_swizzled && blockDim.x == 64)
-      zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T, (int64_t)blockIdx.x * 64 + tid,
-                      (int64_t)gridDim.x * 64);
   }
 }
 
@@ -677,7 +676,7 @@ static bool make_config(int mode, int64_t T, int H, int K, int slices, Config* c
 
 template <int ACT, int MODE, int G, int P, int JMAX>
 static hipError_t launch_one(const Params& p, const Config& c, hipStream_t s) {
-  dim3 grid((unsigned)(c.grid_x * p.T));
+  dim3 grid((unsigned)(c.grid_x * p.T + p.pad_blocks));
   dim3 block(c.G * c.L);
   if (c.nontemporal)
     hipLaunchKernelGGL((finalize_kernel<ACT, MODE, G, P, JMAX, 2>), grid, block, c.lds, s, p);
@@ -826,7 +825,13 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
   Config cfg;
   if (!make_config(mode, c.T, (int)c.H, c.K, slices, &cfg)) return MOE_FIN_ERR_HIDDEN;
   cfg.nontemporal = use_nontemporal(c.T, c.H, c.K);
-  if ((int64_t)cfg.grid_x * c.T > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
+  // swizzled NVFP4 with padding rows: workgroups after the token ones that zero the padding
+  // scale bytes, about two 4-byte words per thread
+  const int pad_blocks =
+      mode == MODE_NVFP4 && sf_layout == MOE_SF_SWIZZLED_128x4 && c.T % 128 != 0
+          ? (int)((((c.H / 16 + 3) / 4) * 128 + 2 * cfg.G * cfg.L - 1) / (2 * cfg.G * cfg.L))
+          : 0;
+  if ((int64_t)cfg.grid_x * c.T + pad_blocks > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
   Params p = base_params(c);
   p.residual = (const uint8_t*)residual;
   p.gamma = (const uint8_t*)gamma;
@@ -842,6 +847,7 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
   p.slices = cfg.grid_x;
   p.ws = (uint8_t*)workspace;
   p.route_stride = route_stride;
+  p.pad_blocks = pad_blocks;
   hipStream_t s = (hipStream_t)stream;
   switch (mode) {
     case MODE_RMS: return to_code(dispatch<MODE_RMS>(c.act, p, cfg, s));
