@@ -602,14 +602,20 @@ static void finish_config(int K, Config* c) {
 // counts, T = 1..256, hidden 1024..16384, top_k 6..22): up to top_k 8 the best slices hold at
 // least 128 slots and give at most one workgroup per CU, min(slots / 128, 256 / T) (hidden 7168:
 // 7 slices at T = 32, 4 at T = 64, 2 at T = 96..128, whole rows from T = 256); with more routes
-// per token, smaller slices of 64 slots and ~224 workgroups, min(slots / 64, 224 / T), win; with
-// four routes or fewer (about five rows of data per token, e.g. a four-rank sum) whole rows win
-// from T = 96 (0.14-0.16 us at T = 96 and 128, hidden 7168). 1 = whole rows (no workspace).
-static int choose_slices(int64_t T, int nv, int K) {
-  if (K <= 4 && T >= 96) return 1;
+// per token, smaller slices of 64 slots and ~224 workgroups, min(slots / 64, 224 / T), win, but
+// no more than 16 of them (hidden 12288..16384 at T = 1..8: 16 slices beat 24-32 by 0.4-1.2 us,
+// the exchange growing with the slices polled); with four routes or fewer (about five rows of
+// data per token, e.g. a four-rank sum) whole rows win from T = 96 (0.14-0.16 us at T = 96 and
+// 128, hidden 7168) for plain RMSNorm, while the quantized outputs keep the split: their epilogue
+// is arithmetic-bound, and a whole row puts it on one CU (NVFP4 at T = 96..128, hidden 7168 and
+// 16384: 1.1-2.2 us faster split; FP8 0.6-2.1 us, within 0.1 us at hidden 4096).
+// 1 = whole rows (no workspace).
+static int choose_slices(int64_t T, int nv, int K, bool quantized) {
+  if (K <= 4 && T >= 96 && !quantized) return 1;
   const int max_by_h = nv / (K > 8 ? 64 : 128);
   int S = (int)((K > 8 ? 224 : 256) / (T > 0 ? T : 1));
   if (S > max_by_h) S = max_by_h;
+  if (K > 8 && S > 16) S = 16;
   if (S > kMaxSlices) S = kMaxSlices;
   for (; S > 1; --S) {
     const int span = ((nv + S - 1) / S + 7) / 8 * 8;
@@ -821,7 +827,7 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
                     float eps, void* residual_out, void* norm_out, const float* qscale,
                     void* quant_out, void* scale_out, int sf_layout, void* workspace,
                     void* stream, int route_stride = 0) {
-  const int slices = workspace ? choose_slices(c.T, (int)(c.H / 8), c.K) : 1;
+  const int slices = workspace ? choose_slices(c.T, (int)(c.H / 8), c.K, mode != MODE_RMS) : 1;
   Config cfg;
   if (!make_config(mode, c.T, (int)c.H, c.K, slices, &cfg)) return MOE_FIN_ERR_HIDDEN;
   cfg.nontemporal = use_nontemporal(c.T, c.H, c.K);
@@ -1034,7 +1040,8 @@ static int entry_config(int entry, int64_t num_tokens, int64_t hidden, int top_k
   if (hidden <= 0 || hidden % 8 != 0 || (entry > 0 && hidden > 16384)) return MOE_FIN_ERR_HIDDEN;
   if (num_tokens < 0 || num_tokens > INT32_MAX / 2) return MOE_FIN_ERR_BAD_SHAPE;
   const int64_t T = num_tokens > 0 ? num_tokens : 1;
-  const int slices = entry > 0 && with_workspace ? choose_slices(T, (int)(hidden / 8), top_k) : 1;
+  const int slices =
+      entry > 0 && with_workspace ? choose_slices(T, (int)(hidden / 8), top_k, entry == 2) : 1;
   if (!make_config(entry == 0 ? MODE_FIN : MODE_RMS, T, (int)hidden, top_k, slices, c))
     return MOE_FIN_ERR_HIDDEN;
   c->nontemporal = use_nontemporal(T, hidden, top_k);

@@ -1019,12 +1019,16 @@ def test_rank_sum_dyadic_bit_exact(act):
     check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, act)
 
 
+@pytest.mark.parametrize("TH", [(64, 6144), (100, 7168)])
 @pytest.mark.parametrize("qt", [M.MOE_QUANT_NVFP4, M.MOE_QUANT_FP8_E4M3])
-def test_rank_sum_quant(qt):
+def test_rank_sum_quant(qt, TH):
     """Rank sum + residual + RMSNorm + quantization: codes and scales bit-exact against the
-    oracle's quantization of the kernel's own norm_out (which meets the norm_out bar)."""
-    T, W, H = 64, 4, 6144
-    inp = _rank_sum_inputs(T, H, W, "bf16", seed=6200)
+    oracle's quantization of the kernel's own norm_out (which meets the norm_out bar). At 100
+    tokens and four partials the quantized call splits rows where plain RMSNorm takes whole rows,
+    and the swizzled scales have padding rows."""
+    T, H = TH
+    W = 4
+    inp = _rank_sum_inputs(T, H, W, "bf16", seed=6200 + T)
     ref = oracle_ref(inp)
     P_ = inp.rows.view(W, T, H).cuda()
     nv = qt == M.MOE_QUANT_NVFP4
