@@ -606,12 +606,13 @@ static void finish_config(int K, Config* c) {
 // no more than 16 of them (hidden 12288..16384 at T = 1..8: 16 slices beat 24-32 by 0.4-1.2 us,
 // the exchange growing with the slices polled); with four routes or fewer (about five rows of
 // data per token, e.g. a four-rank sum) whole rows win from T = 96 (0.14-0.16 us at T = 96 and
-// 128, hidden 7168) for plain RMSNorm, while the quantized outputs keep the split: their epilogue
-// is arithmetic-bound, and a whole row puts it on one CU (NVFP4 at T = 96..128, hidden 7168 and
-// 16384: 1.1-2.2 us faster split; FP8 0.6-2.1 us, within 0.1 us at hidden 4096).
-// 1 = whole rows (no workspace).
+// 128, hidden 7168) for plain RMSNorm while a token's rows, shared and residual slices stay
+// within 128 KiB for its CU (hidden 16384 top_k 4 split: 1.0-1.2 us faster at T = 96..128), while
+// the quantized outputs keep the split: their epilogue is arithmetic-bound, and a whole row puts
+// it on one CU (NVFP4 at T = 96..128, hidden 7168 and 16384: 1.1-2.2 us faster split; FP8
+// 0.6-2.1 us, within 0.1 us at hidden 4096). 1 = whole rows (no workspace).
 static int choose_slices(int64_t T, int nv, int K, bool quantized) {
-  if (K <= 4 && T >= 96 && !quantized) return 1;
+  if (K <= 4 && T >= 96 && !quantized && (K + 2) * nv * 16 <= (128 << 10)) return 1;
   const int max_by_h = nv / (K > 8 ? 64 : 128);
   int S = (int)((K > 8 ? 224 : 256) / (T > 0 ? T : 1));
   if (S > max_by_h) S = max_by_h;

@@ -655,7 +655,7 @@ def test_quantize_nonfinite_bit_exact(act):
 # ---- large batches (prefill-sized calls: whole rows, nontemporal streaming) ---------------------
 @pytest.mark.parametrize("THK", [(256, 7168, 8), (512, 7168, 8), (2048, 2048, 8), (300, 3584, 16),
                                  (1024, 7168, 8), (1030, 5120, 8), (1024, 3584, 16),
-                                 (1024, 7168, 4), (1024, 7168, 16)])
+                                 (1024, 7168, 4), (1024, 7168, 16), (100, 16384, 4)])
 def test_large_batch(THK):
     """From 1024 tokens whole-row workgroups are rounded up to four wavefronts (hidden 7168: 1024
     lanes for 896 slots; 5120: 768 for 640), so their last lanes hold no slot."""
