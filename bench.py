@@ -118,6 +118,8 @@ def _parse():
                    help="input copies rotated per graph (96 x 22 MB = 2.1 GB, 8x the Infinity Cache)")
     p.add_argument("--sweep", action="store_true")
     p.add_argument("--no-large", action="store_true", help="sweep without the T >= 256 cases")
+    p.add_argument("--scan", action="store_true",
+                   help="warm timings over a grid of uncommon shapes (performance-cliff check)")
     p.add_argument("--groups", default="", help="comma-separated sweep groups to run (default all)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -251,6 +253,8 @@ def main():
         out["cases"] = _sweep(torch, M, stream, dev, large=not a.no_large,
                               groups=[g for g in a.groups.split(",") if g],
                               cpu=not a.no_cpu_baseline)
+    if a.scan:
+        out["scan"] = _scan(torch, M, stream, dev)
     out["workspace_flag"] = int(ws[:4].view(torch.int32).item())
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, nbytes, a.cpu_seconds)
@@ -315,6 +319,53 @@ def _warm_us(torch, stream, fn, launches=20, replays=50):
     """The pages' protocol: one graph of `launches` calls on the same inputs, median of
     `replays` replays, µs per call."""
     return _graph_us(torch, stream, [fn] * launches, replays)
+
+
+def _scan(torch, M, stream, dev):
+    """Warm µs per call (the pages' protocol, 15 replays) over a grid of shapes outside the
+    measured workloads: tokens 1..250, hidden 1024..16384, top_k 1..64, for the finalize, RMSNorm,
+    NVFP4 (swizzled scales, norm_out not stored) and FP8 entry points, with the RMSNorm launch
+    floor. A check for performance cliffs; inputs are drawn on the device (bf16, fp32 scales,
+    shared expert, a quarter of the routes absent) and the per-tensor scale is fixed at 100."""
+    from synth import make_inputs_on_device
+    ws = torch.zeros(M.moe_finalize_workspace_size(256, 0, 0), dtype=torch.uint8, device=dev)
+    qs = torch.tensor([100.0], dtype=torch.float32, device=dev)
+    swz = M.MOE_SF_SWIZZLED_128x4
+    recs = []
+    for T in (1, 3, 16, 100, 250):
+        for H in (1024, 4096, 7168, 16384):
+            for K in (1, 4, 8, 22, 64):
+                print(f"scan T={T} H={H} K={K}", file=sys.stderr, flush=True)
+                i = make_inputs_on_device(T, H, K, seed=9000 + T, device=dev)
+                ro = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+                no = torch.empty_like(ro)
+                q4 = torch.empty(T, H // 2, dtype=torch.uint8, device=dev)
+                q8 = torch.empty(T, H, dtype=torch.uint8, device=dev)
+                sf = torch.empty(M.moe_finalize_sf_size(T, H, swz), dtype=torch.uint8, device=dev)
+                calls = {
+                    "finalize": lambda: M.moe_finalize_run(i.rows, i.idx, i.scales, i.shared, i.rsf,
+                                                           no, stream=stream),
+                    "rmsnorm": lambda: M.moe_finalize_rmsnorm_run(
+                        i.rows, i.idx, i.scales, i.shared, i.rsf, i.residual, i.gamma, i.eps, ro,
+                        no, ws, stream=stream),
+                    "nvfp4": lambda: M.moe_finalize_quant_run(
+                        i.rows, i.idx, i.scales, i.shared, i.rsf, i.residual, i.gamma, i.eps,
+                        M.MOE_QUANT_NVFP4, qs, q4, sf, swz, ro, None, ws, stream=stream),
+                    "fp8": lambda: M.moe_finalize_quant_run(
+                        i.rows, i.idx, i.scales, i.shared, i.rsf, i.residual, i.gamma, i.eps,
+                        M.MOE_QUANT_FP8_E4M3, qs, q8, None, 0, ro, None, ws, stream=stream),
+                    "floor": lambda: M.moe_finalize_launch_floor_run(1, T, H, K, device=dev,
+                                                                     stream=stream),
+                }
+                r = {"T": T, "H": H, "K": K,
+                     "bytes_rmsnorm": algorithmic_bytes(T, H, K, int((i.idx >= 0).sum()), 4, True,
+                                                        "rmsnorm")}
+                for name, fn in calls.items():
+                    r[name] = round(_warm_us(torch, stream, fn, replays=15), 3)
+                recs.append(r)
+                del i, ro, no, q4, q8, sf
+    assert int(ws[:4].view(torch.int32).item()) == 0, "a split row timed out in the scan"
+    return recs
 
 
 # Sweep cases: (group, entry, T, H, K, act, scales, shared, quant). entry: "rmsnorm" (fused
