@@ -1,0 +1,62 @@
+"""Host logic of bench.py (no GPU): the algorithmic byte model behind every reported GB/s and
+roofline figure, and the code hash that ties the committed traffic counters to the kernels."""
+from __future__ import annotations
+
+import os
+import sys
+
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+import bench  # noqa: E402
+
+
+def _valid(T, K):
+    # a quarter of the routes absent, as the generators draw them
+    return T * K - (T * K) // 4
+
+
+# (T, H, K, entry, extra kwargs, bytes): reads = valid rows + route metadata (int32 index and
+# float32 scale) + shared + residual + gamma; writes = residual_out + norm_out (finalize only: its
+# output; quantized: residual_out + codes + block scales with the 128x4 padding), worked out by
+# hand for the decode workloads.
+CASES = [
+    (4, 1024, 8, "rmsnorm", {}, 84_224),
+    (1, 6144, 8, "rmsnorm", {}, 135_232),
+    (4, 6144, 8, "rmsnorm", {}, 504_064),
+    (16, 6144, 8, "rmsnorm", {}, 1_979_392),
+    (32, 7168, 8, "rmsnorm", {}, 4_603_904),
+    (64, 7168, 8, "rmsnorm", {}, 9_193_472),
+    (128, 7168, 8, "rmsnorm", {}, 18_372_608),
+    (1, 2048, 22, "finalize", {"shared": False}, 73_904),
+    (32, 2048, 22, "finalize", {"shared": False}, 2_299_392),
+    (1, 3584, 16, "finalize", {"shared": False}, 93_312),
+    (32, 3584, 16, "finalize", {"shared": False}, 2_985_984),
+    (64, 6144, 8, "quant", {"quant": "nvfp4", "norm_out": False}, 7_340_032),
+    (64, 6144, 8, "quant", {"quant": "fp8", "norm_out": False}, 7_487_488),
+    (64, 6144, 8, "rmsnorm", {}, 7_880_704),
+]
+
+
+@pytest.mark.parametrize("T,H,K,entry,kw,want", CASES)
+def test_algorithmic_bytes(T, H, K, entry, kw, want):
+    shared = kw.pop("shared", True)
+    assert bench.algorithmic_bytes(T, H, K, _valid(T, K), 4, shared, entry, **kw) == want
+
+
+def test_headline_bytes_split():
+    """The headline's reads and writes add up to its algorithmic bytes; the writes are the two
+    [T, H] bf16 outputs."""
+    T, H, K = 128, 7168, 8
+    total = bench.algorithmic_bytes(T, H, K, _valid(T, K))
+    reads = bench._read_bytes(T, H, K, _valid(T, K))
+    assert total - reads == 2 * T * H * 2
+
+
+def test_code_hash_ignores_comments_only():
+    a = "int f(int x) {  // the sum\n  return x + 1; /* one */ }\n"
+    b = "int f(int x) {\n  // a different comment\n  return x + 1;\n}\n"
+    c = "int f(int x) { return x + 2; }\n"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+    assert len(bench.kernel_source_hash()) >= 16
