@@ -392,6 +392,8 @@ def _sweep_cases(large):
     # one GPU's share of the cross-rank reduction at the pages' TP4 shapes (world size 4)
     c += [("ranksum", "rank_sum", t, h, 4, "bf16", None, False, None)
           for (h, ts) in ((6144, (1, 16)), (7168, (1, 16, 64, 128))) for t in ts]
+    c += [("ranksum", "rank_sum_quant", t, h, 4, "bf16", None, False, q)
+          for h in (6144, 7168) for t in (1, 16) for q in ("nvfp4", "fp8")]
     if large:
         c += [("batch", e, t, 7168, 8, "bf16", "fp32", True, None) for t in (256, 512, 1024, 2048)
               for e in ("rmsnorm", "finalize")]
@@ -415,18 +417,24 @@ def _sweep(torch, M, stream, dev, large=True, groups=(), cpu=False):
         kvar = K if grp == "highk" else None
         inp = make_inputs(T, H, K, act_dtype=act, scale_dtype=sdt, with_shared=sh,
                           seed=workload_seed(grp, T, act, sdt, kvar),
-                          mask_frac=0.0 if entry == "rank_sum" else 0.25)
+                          mask_frac=0.0 if entry.startswith("rank_sum") else 0.25)
         n_valid = int((inp.idx >= 0).sum())
         dt = inp.rows.dtype
         qkind = (quant or "").split("+")[0]
         keep_norm = quant is None or quant.endswith("+norm")
         q_scale = None
-        if entry.startswith("quant"):
+        if entry.startswith("quant") or entry == "rank_sum_quant":
             # the caller's per-tensor scale from the tensor's amax (448*6/amax or 448/amax)
             probe = _dev_set(torch, inp, dev)
-            M.moe_finalize_rmsnorm_run(probe["rows"], probe["idx"], probe["scales"],
-                                       probe["shared"], inp.rsf, probe["residual"],
-                                       probe["gamma"], inp.eps, probe["ro"], probe["no"], ws_big)
+            if entry == "rank_sum_quant":
+                M.moe_rank_sum_rmsnorm_run(probe["rows"].view(inp.K, inp.T, inp.H),
+                                           probe["residual"], probe["gamma"], inp.eps,
+                                           probe["ro"], probe["no"], ws_big)
+            else:
+                M.moe_finalize_rmsnorm_run(probe["rows"], probe["idx"], probe["scales"],
+                                           probe["shared"], inp.rsf, probe["residual"],
+                                           probe["gamma"], inp.eps, probe["ro"], probe["no"],
+                                           ws_big)
             amax = float(probe["no"].float().abs().max())
             q_scale = torch.tensor([(2688.0 if qkind.startswith("nvfp4") else 448.0) / amax],
                                    dtype=torch.float32, device=dev)
@@ -458,6 +466,11 @@ def _sweep(torch, M, stream, dev, large=True, groups=(), cpu=False):
                 return f
             qt = M.MOE_QUANT_FP8_E4M3 if qkind == "fp8" else M.MOE_QUANT_NVFP4
             lay = M.MOE_SF_LINEAR if qkind == "nvfp4_linear" else M.MOE_SF_SWIZZLED_128x4
+            if entry == "rank_sum_quant":
+                parts = d["rows"].view(inp.K, inp.T, inp.H)
+                return lambda: M.moe_rank_sum_quant_run(parts, d["residual"], d["gamma"], inp.eps,
+                                                        qt, q_scale, d["q"], d.get("sf"), lay,
+                                                        d["ro"], None, ws_big, stream=stream)
             if entry == "quant_two_kernel":
                 # the unfused alternative: finalize + residual + RMSNorm, then quantize norm_out
                 def f2():
@@ -472,7 +485,8 @@ def _sweep(torch, M, stream, dev, large=True, groups=(), cpu=False):
                 d["gamma"], inp.eps, qt, q_scale, d["q"], d.get("sf"), lay, d["ro"],
                 d["no"] if keep_norm else None, ws_big, stream=stream)
 
-        floor_entry = {"finalize": 0, "rmsnorm": 1, "quant": 2, "rank_sum": 1}.get(entry, 1)
+        floor_entry = {"finalize": 0, "rmsnorm": 1, "quant": 2, "rank_sum": 1,
+                       "rank_sum_quant": 2}.get(entry, 1)
         if entry in ("two_kernel", "quant_two_kernel"):
             def floor_fn(T=T, H=H, K=K):                 # two empty launches
                 M.moe_finalize_launch_floor_run(0, T, H, K, device=dev, stream=stream)
@@ -485,6 +499,11 @@ def _sweep(torch, M, stream, dev, large=True, groups=(), cpu=False):
         base_entry = {"two_kernel": "rmsnorm", "quant_two_kernel": "quant"}.get(entry, entry)
         if entry == "rank_sum":
             nb = _read_bytes(T, H, K, n_valid, entry="rank_sum") + 2 * T * H * ACT_BYTES
+        elif entry == "rank_sum_quant":
+            # the rank sum's reads, the quantized entry's writes (residual_out, codes, scales)
+            wr = (algorithmic_bytes(T, H, K, n_valid, 4, False, "quant", quant=qkind,
+                                    norm_out=False) - _read_bytes(T, H, K, n_valid, 4, False, "quant"))
+            nb = _read_bytes(T, H, K, n_valid, entry="rank_sum") + wr
         else:
             nb = algorithmic_bytes(T, H, K, n_valid, 4 if sdt == "fp32" else 2, sh, base_entry,
                                    quant=qkind or None, norm_out=keep_norm)
