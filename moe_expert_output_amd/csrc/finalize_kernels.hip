@@ -109,7 +109,10 @@ struct QuantDst {
 // through `q_r` (the row's code buffer); for NVFP4 also the block scales. Every lane of the
 // wavefront must call it (the NVFP4 block amax and scale gathers are cross-lane). Lanes with
 // live == false hold zeros and store nothing.
-template <int MODE>
+// NTQ: the aux bits of the FP8 code stores (the fused kernel passes its nontemporal choice:
+// same-box A/B, cold, FP8 at T = 64 / 128 / 512: 0.18 / 0.35 / 0.58 us faster; the NVFP4 code
+// stores, 4 bytes per lane, stay cacheable: nontemporal was 0.37 us slower at T = 512).
+template <int MODE, int NTQ = 0>
 __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
                                                const __amdgpu_buffer_rsrc_t& q_r, uint32_t voff,
                                                bool live, int s, int t, const QuantDst& d) {
@@ -122,7 +125,7 @@ __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
       const uint32_t c = e4m3_code(__builtin_fabs((double)nr[e]) * qs) | (sgn << 7);
       q[e >> 2] |= c << (8 * (e & 3));
     }
-    __builtin_amdgcn_raw_buffer_store_b64(q, q_r, voff >> 1, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(q, q_r, voff >> 1, 0, NTQ);
   } else {
     // NVFP4: a 16-element block is this lane's 8 elements and the neighbouring lane's 8.
     // A NaN anywhere in the block makes its amax NaN: scale code 0x7F and all-zero codes.
@@ -193,8 +196,8 @@ __device__ __forceinline__ void zero_sf_padding(const QuantDst& d, int T, int64_
 }
 
 // NT = 2 marks the streamed accesses nontemporal (chosen for large calls): the row, shared and
-// residual loads and the residual_out and norm_out stores; gamma, shared by every token, stays
-// cacheable. NT = 0 leaves them all cacheable.
+// residual loads, the residual_out and norm_out stores and the FP8 code stores; gamma, shared by
+// every token, stays cacheable. NT = 0 leaves them all cacheable.
 template <int ACT, int MODE, int G, int P, int JMAX, int NT>
 __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   // blockIdx.x = token * slices + slice (one slice per token in the whole-row modes). For NVFP4
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) {
       float nr[8];
       Act<ACT>::unpack(n_pk, nr);               // quantize the rounded norm_out values
-      quantize_store<MODE>(nr, qs, q_r, voff[p], live[p], slot0 + lane + p * L, t,
+      quantize_store<MODE, NT>(nr, qs, q_r, voff[p], live[p], slot0 + lane + p * L, t,
                            QuantDst{a.sf_out, a.H, a.sf_swizzled});
     }
   }
