@@ -4,8 +4,10 @@ Default workload (one "step" = one call of the whole path over one decode batch)
 hidden 7168, top-8 routes with a quarter of them marked -1, float32 softmax expert scales, RSF
 2.5, shared-expert add, residual add and RMSNorm (eps 1e-6), bf16 activations, seeded synthetic
 inputs resident in HBM. Each timed call reads a different copy of the inputs, rotating over 2.1 GB
-(8x the 256 MiB Infinity Cache), so every input comes from HBM (cold). The calls are captured in a
-HIP graph and replayed; HIP events on the launch stream bracket exactly K calls.
+(8x the 256 MiB Infinity Cache), so every input comes from HBM (cold). Every call is a HIP graph
+node: a warm-up graph over all copies is replayed first, then a graph of exactly K calls is
+replayed once between two HIP events on the launch stream (timing_plan); nothing is launched
+eagerly in the timed region, whatever K is.
 
 Output: one JSON line (metric, value = achieved algorithmic GB/s, us/call, roofline of the
 finalize kernel, the FP64 CPU oracle's throughput on the host as a baseline). Beside the HBM
@@ -109,11 +111,31 @@ def algorithmic_bytes(T, H, K, n_valid, scale_bytes=4, shared=True, entry="rmsno
     return rd + 2 * T * H * e
 
 
+def timing_plan(steps: int, warmup: int, n_sets: int) -> dict:
+    """How the headline run spends its calls; every call is a graph-node launch, none is eager.
+
+    Timed: a graph of exactly `steps` calls on copies 0, 1, ..., n_sets - 1, 0, 1, ... replayed
+    ONCE between the two events. Before that, untimed: that graph is replayed once (its first
+    replay also uploads it to the device, a one-time cost of ~10 us that would otherwise land in
+    the timed region), then a graph that makes one call on each of the n_sets copies in order is
+    replayed ceil(warmup / n_sets) times (at least once), so at least `warmup` calls run untimed.
+    Copy i was last read n_sets - i calls before the timed graph reads it (the warm-up ends on
+    copy n_sets - 1), and n_sets copies are 8x the Infinity Cache, so every timed call reads its
+    inputs from HBM."""
+    if steps < 1 or n_sets < 1 or warmup < 0:
+        raise ValueError("steps >= 1, warmup >= 0 and n_sets >= 1 are required")
+    replays = max(1, -(-warmup // n_sets))
+    timed = [i % n_sets for i in range(steps)]
+    return {"upload_replay_sets": timed, "warmup_sets": list(range(n_sets)),
+            "warmup_replays": replays, "warmup_calls": steps + replays * n_sets,
+            "timed_sets": timed, "timed_replays": 1, "timed_calls": steps, "eager_calls": 0}
+
+
 def _parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=3200)
-    p.add_argument("--warmup", type=int, default=320)
+    p.add_argument("--steps", type=int, default=960)
+    p.add_argument("--warmup", type=int, default=192)
     p.add_argument("--sets", type=int, default=96,
                    help="input copies rotated per graph (96 x 22 MB = 2.1 GB, 8x the Infinity Cache)")
     p.add_argument("--sweep", action="store_true")
@@ -161,7 +183,8 @@ def main():
                                    d["residual"], d["gamma"], inp.eps, d["res_out"],
                                    d["norm_out"], ws)
 
-    # Capture one graph that calls the path once on every input copy.
+    # Warm-up: one graph that calls the path once on every input copy, replayed. Timed: a second
+    # graph of exactly K calls over the copies in the same order (see timing_plan), replayed once.
     stream = torch.cuda.Stream(device=dev)
     stream.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(stream):
@@ -169,29 +192,32 @@ def main():
             call(d)
     torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for d in sets:
-            call(d)
-
     n_sets = len(sets)
     K_steps, W = int(a.steps), int(a.warmup)
+    plan = timing_plan(K_steps, W, n_sets)
+    warm_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(warm_graph, stream=stream):
+        for i in plan["warmup_sets"]:
+            call(sets[i])
+    timed_graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(timed_graph, stream=stream):
+        for i in plan["timed_sets"]:
+            call(sets[i])
     with torch.cuda.stream(stream):
-        for _ in range(max(1, W // n_sets)):
-            graph.replay()
+        timed_graph.replay()                       # untimed: uploads the timed graph
+        for _ in range(plan["warmup_replays"]):
+            warm_graph.replay()
         torch.cuda.synchronize()
         t_host0 = time.perf_counter()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
         ev0.record(stream)
-        for _ in range(K_steps // n_sets):
-            graph.replay()
-        for i in range(K_steps % n_sets):          # remainder, launched directly
-            call(sets[i])
+        timed_graph.replay()
         ev1.record(stream)
         ev1.synchronize()
         t_host1 = time.perf_counter()
     torch.cuda.synchronize()
+    del warm_graph, timed_graph
     us_per_call = ev0.elapsed_time(ev1) * 1e3 / K_steps
     gbs = nbytes / (us_per_call * 1e-6) / 1e9
 
@@ -240,6 +266,8 @@ def main():
         "launch_floor_us": round(floor, 3),
         "algorithmic_bytes_per_call": nbytes,
         "host_wall_s": round(t_host1 - t_host0, 4),
+        "timing": {"warmup_calls": plan["warmup_calls"], "timed_graph_calls": plan["timed_calls"],
+                   "timed_graph_replays": plan["timed_replays"], "eager_calls": plan["eager_calls"]},
         "plain_copy_same_bytes_us": round(copy_us, 3),
         "stream_ceiling_same_bytes_us": round(ceil_us, 3),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_GBS, "unit": "GB/s",

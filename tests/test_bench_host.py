@@ -60,3 +60,35 @@ def test_code_hash_ignores_comments_only():
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only(c)
     assert len(bench.kernel_source_hash()) >= 16
+
+
+@pytest.mark.parametrize("steps", [1, 2, 19, 20, 95, 96, 97, 192, 960, 3201])
+@pytest.mark.parametrize("warmup", [0, 1, 5, 96, 320])
+def test_timing_plan_is_graph_replays_only(steps, warmup):
+    """The headline's timed region is one replay of a graph of exactly `steps` calls for every
+    steps >= 1 (no eager remainder), over the input copies in the order the warm-up graph read
+    them, and the warm-up makes at least `warmup` calls."""
+    n_sets = 96
+    plan = bench.timing_plan(steps, warmup, n_sets)
+    assert plan["eager_calls"] == 0
+    assert plan["timed_replays"] == 1 and plan["timed_calls"] == steps
+    assert len(plan["timed_sets"]) == steps
+    assert plan["timed_sets"][:min(steps, n_sets)] == list(range(min(steps, n_sets)))
+    assert all(0 <= i < n_sets for i in plan["timed_sets"])
+    # every timed call reads a copy whose previous read was n_sets calls earlier (cold rotation:
+    # the other n_sets - 1 copies were read in between)
+    pre = plan["upload_replay_sets"] + plan["warmup_sets"] * plan["warmup_replays"]
+    seq = pre + plan["timed_sets"]
+    last = {}
+    for pos, i in enumerate(seq):
+        if pos >= len(pre):
+            assert pos - last[i] == n_sets
+        last[i] = pos
+    assert plan["upload_replay_sets"] == plan["timed_sets"]
+    assert plan["warmup_calls"] >= max(warmup, 1)
+    assert plan["warmup_calls"] == steps + plan["warmup_replays"] * n_sets
+
+
+def test_timing_plan_rejects_empty_runs():
+    with pytest.raises(ValueError):
+        bench.timing_plan(0, 5, 96)
