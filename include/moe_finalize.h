@@ -53,12 +53,17 @@
  *     (no per-call clearing, so graph replays need no memset node). Calls that may run at the
  *     same time (different streams) must use different workspaces. Its first 32-bit word is a
  *     sticky flag that a kernel sets to nonzero if a workgroup gave up waiting for the other
- *     slices of its row (outputs of that call are then unreliable); it stays 0 in normal use.
+ *     slices of its row; it stays 0 in normal use. A workgroup that gives up counts the missing
+ *     partial sums as NaN, so its part of that token's norm_out is NaN (FP8 codes 0x7F; NVFP4
+ *     block scales 0x7F with zero codes) instead of a wrong finite value; residual_out is not
+ *     affected. After the flag is set, zero the workspace again before its next use.
  *     Progress: a token's slices are consecutive workgroups and rows are split only while the
- *     grid stays near one workgroup per CU, so workgroups dispatched before a waiting one never
- *     wait on it (the scale-padding workgroups of an NVFP4 call come last and wait on nothing)
- *     and the slices of a row run together. The wait is bounded (about a second)
- *     even if other work were to hold every CU; the flag then reports it.
+ *     grid stays near one workgroup per compute unit of the current device (its count is
+ *     queried once per device), so workgroups dispatched before a waiting one never wait on it
+ *     (the scale-padding workgroups of an NVFP4 call come last and wait on nothing) and the
+ *     slices of a row run together. The wait is bounded (about a second, see
+ *     moe_finalize_set_wait_limit) even if other work were to hold every CU; the flag and the
+ *     NaN outputs then report it.
  */
 #ifndef MOE_FINALIZE_H_
 #define MOE_FINALIZE_H_
@@ -178,7 +183,7 @@ int moe_finalize_quant_run(const void* permuted_rows, int64_t num_permuted_rows,
 
 /*
  * moe_finalize_workspace_size -- bytes of workspace the RMSNorm entry points may use for a call
- * with this shape (256 + 512 per token). Host-only. Returns 0 for num_tokens < 0.
+ * with this shape (256 + 256 per token). Host-only. Returns 0 for num_tokens < 0.
  */
 size_t moe_finalize_workspace_size(int64_t num_tokens, int64_t hidden, int top_k);
 
@@ -276,8 +281,10 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
 /*
  * moe_finalize_launch_config -- the launch configuration entry point `entry` (0 =
  * moe_finalize_run, 1 = moe_finalize_rmsnorm_run, 2 = moe_finalize_quant_run) chooses for a shape,
- * with (with_workspace != 0) or without a workspace. Host-only, never touches the GPU. Writes
- * MOE_FIN_LAUNCH_CONFIG_FIELDS int64 values to `out` (n_out is the caller's array length):
+ * with (with_workspace != 0) or without a workspace, on a device of `num_cus` compute units
+ * (num_cus <= 0: the current device's count, which only this case queries; with a workspace the
+ * slice rule depends on it). Host-only; launches nothing. Writes MOE_FIN_LAUNCH_CONFIG_FIELDS
+ * int64 values to `out` (n_out is the caller's array length):
  *   out[0] workgroups in the grid (0 when num_tokens == 0); a swizzled NVFP4 call whose
  *          num_tokens is not a multiple of 128 adds a few workgroups after these that only
  *          zero the scale bytes of the padding rows
@@ -291,7 +298,8 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
  *   out[8] 1 when the library holds a kernel for this configuration
  * Returns the entry point's shape-validation code (an unknown `entry` gives
  * MOE_FIN_ERR_QUANT_TYPE), MOE_FIN_ERR_NULL_POINTER for out == NULL, MOE_FIN_ERR_BAD_SHAPE when
- * n_out < MOE_FIN_LAUNCH_CONFIG_FIELDS.
+ * n_out < MOE_FIN_LAUNCH_CONFIG_FIELDS, MOE_FIN_ERR_HIP when num_cus <= 0 and the device count
+ * cannot be queried.
  */
 #define MOE_FIN_LAUNCH_CONFIG_FIELDS 9
 
@@ -307,14 +315,26 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
  * moe_finalize_run never stores its output nontemporally. Results are bit-identical under every
  * policy. The policy is read when a call is enqueued, so a captured graph keeps the choice made
  * at capture. Returns the previous policy, or MOE_FIN_ERR_POLICY for an unknown value (the
- * policy is then unchanged). This is the library's only process-wide setting.
+ * policy is then unchanged). Besides the wait limit below, this is the library's only
+ * process-wide setting.
  */
 #define MOE_FIN_CACHE_AUTO 0
 #define MOE_FIN_CACHE_KEEP 1
 #define MOE_FIN_CACHE_STREAM 2
 int moe_finalize_set_cache_policy(int policy);
 int moe_finalize_launch_config(int entry, int64_t num_tokens, int64_t hidden, int top_k,
-                               int with_workspace, int64_t* out, int n_out);
+                               int with_workspace, int num_cus, int64_t* out, int n_out);
+
+/*
+ * moe_finalize_set_wait_limit -- how many times a workgroup of a split row polls for the other
+ * slices' partial sums before it gives up (sets the workspace flag and writes NaN, see
+ * "Workspace"). polls < 0 restores the default (4194304 polls, about 0.1-0.5 s); values above
+ * 2^32 - 1 are clamped. 0 makes every split-row wait give up at once, which lets a caller check
+ * its handling of a timed-out call without any GPU fault or hang. Process-wide, read when a
+ * call is enqueued (a captured graph keeps the limit of its capture). Host-only. Returns the
+ * previous limit.
+ */
+int64_t moe_finalize_set_wait_limit(int64_t polls);
 
 /*
  * moe_finalize_stream_floor_run -- measurement aid: read `read_bytes` from `src` and write

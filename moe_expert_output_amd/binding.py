@@ -26,7 +26,7 @@ EXPORTED = ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_
             "moe_finalize_launch_floor_run", "moe_finalize_workspace_size", "moe_quantize_run",
             "moe_residual_rmsnorm_run", "moe_finalize_stream_floor_run",
             "moe_rank_sum_rmsnorm_run", "moe_rank_sum_quant_run", "moe_finalize_launch_config",
-            "moe_finalize_set_cache_policy")
+            "moe_finalize_set_cache_policy", "moe_finalize_set_wait_limit")
 
 _ACT = {torch.bfloat16: MOE_DTYPE_BF16, torch.float16: MOE_DTYPE_FP16}
 _SCALE = {torch.float32: MOE_DTYPE_FP32, torch.bfloat16: MOE_DTYPE_BF16}
@@ -66,11 +66,13 @@ def _load() -> ctypes.CDLL:
     lib.moe_finalize_version.restype = ctypes.c_int
     lib.moe_finalize_launch_floor_run.argtypes = [i32, i64, i64, i32, vp]
     lib.moe_finalize_launch_floor_run.restype = ctypes.c_int
-    lib.moe_finalize_launch_config.argtypes = [i32, i64, i64, i32, i32,
+    lib.moe_finalize_launch_config.argtypes = [i32, i64, i64, i32, i32, i32,
                                                ctypes.POINTER(ctypes.c_int64), i32]
     lib.moe_finalize_launch_config.restype = ctypes.c_int
     lib.moe_finalize_set_cache_policy.argtypes = [i32]
     lib.moe_finalize_set_cache_policy.restype = ctypes.c_int
+    lib.moe_finalize_set_wait_limit.argtypes = [i64]
+    lib.moe_finalize_set_wait_limit.restype = i64
     lib.moe_finalize_stream_floor_run.argtypes = [vp, sz, vp, sz, vp]
     lib.moe_finalize_stream_floor_run.restype = ctypes.c_int
     lib.moe_rank_sum_rmsnorm_run.argtypes = [vp, i32, vp, vp, f32, vp, vp, vp, sz, i64, i64, i32,
@@ -121,13 +123,13 @@ LAUNCH_CONFIG_FIELDS = ("workgroups", "lanes", "slices", "route_groups", "slots_
 
 
 def moe_finalize_launch_config(entry: int, num_tokens: int, hidden: int, top_k: int,
-                               with_workspace: bool = True) -> dict:
+                               with_workspace: bool = True, num_cus: int = 0) -> dict:
     """The launch configuration entry point `entry` (0 finalize, 1 RMSNorm, 2 quantized) uses
-    for a shape (host only; raises MoeFinalizeError with the entry point's code for a bad
-    shape)."""
+    for a shape on a device of `num_cus` compute units (0: the current device's; host only;
+    raises MoeFinalizeError with the entry point's code for a bad shape)."""
     out = (ctypes.c_int64 * len(LAUNCH_CONFIG_FIELDS))()
     _check(LIB.moe_finalize_launch_config(int(entry), int(num_tokens), int(hidden), int(top_k),
-                                          1 if with_workspace else 0, out,
+                                          1 if with_workspace else 0, int(num_cus), out,
                                           len(LAUNCH_CONFIG_FIELDS)))
     return dict(zip(LAUNCH_CONFIG_FIELDS, (int(v) for v in out)))
 
@@ -139,6 +141,12 @@ def moe_finalize_set_cache_policy(policy: int) -> int:
     if prev < 0:
         raise MoeFinalizeError(prev, moe_finalize_error_string(prev))
     return prev
+
+
+def moe_finalize_set_wait_limit(polls: int) -> int:
+    """Set the process-wide poll limit of split-row waits (< 0: the default); returns the
+    previous limit."""
+    return int(LIB.moe_finalize_set_wait_limit(int(polls)))
 
 
 def moe_finalize_stream_floor_run(src: torch.Tensor, read_bytes: int, dst: torch.Tensor,

@@ -68,21 +68,30 @@ struct Params {
   int route_stride;          // > 0: no route map; route k of token t is row k * route_stride + t
   int pad_blocks;            // NVFP4, swizzled scales: workgroups after the token ones that
                              // only zero the scale bytes of the padding rows
+  uint32_t spin_limit;       // split rows: polls of a slice's word before the wait gives up
 };
 
 // Split rows. When a token's row is spread over `slices` workgroups, each workgroup publishes
 // the sum of squares of its slice in the caller's workspace and waits for the other slices of
 // its token. Layout: a 256-byte header whose first word is a sticky timeout flag, then one
-// 512-byte block per token holding kMaxSlices 64-bit slots. A slot carries (epoch << 32 |
-// float bits of a partial) in ONE relaxed device-scope atomic word, so the flag and the data
-// become visible together and no release/acquire fences (L2 writeback / invalidate) are needed.
-// All kMaxSlices slots of a token hold the same epoch between calls: slice j rewrites every slot
-// m with m % slices == j, so a call reads the current epoch from its own slot and waits until
-// slots 0..slices-1 carry epoch + 1. A zero-filled workspace is valid, no call needs a reset, and
-// the slice count may change from call to call.
-constexpr int kMaxSlices = 64;
-constexpr size_t kWsHeader = 256, kWsPerToken = 8 * kMaxSlices;
+// 256-byte block per token: kMaxSlices 64-bit slots (bytes 0..127, one cache line) and the
+// token's 32-bit epoch word (byte 128, a line of its own). A slot carries (epoch << 32 | float
+// bits of a partial) in ONE relaxed device-scope atomic word, so the flag and the data become
+// visible together and no release/acquire fences (L2 writeback / invalidate) are needed. Every
+// slice of a call reads the token's epoch E at its start, publishes E + 1 in its own slot and
+// waits until slots 0..slices-1 carry E + 1; after its wait, slice 0 stores E + 1 as the token's
+// epoch. That store comes after every slice has read E (each published E + 1, which depends on
+// its read), and the next call on the stream starts after this one ends, so each call sees the
+// epoch the previous one left. A slot holds at most the token's current epoch between calls, so
+// stale slots of a call with more slices never match. A zero-filled workspace is valid, no call
+// needs a reset, the slice count may change from call to call, and a call writes only the slots
+// it uses and one epoch word per token. When a slice gives up waiting (spin_limit polls), it
+// sets the header flag and counts the missing partials as NaN, so its part of norm_out (and of
+// the quantized outputs) is NaN rather than a wrong finite value; residual_out is unaffected.
+constexpr int kMaxSlices = 16;
+constexpr size_t kWsHeader = 256, kWsPerToken = 256, kWsEpochOffset = 128;
 constexpr uint32_t kMaxSpins = 1u << 22;      // ~0.1-0.5 s of polling, then give up (flagged)
+constexpr uint32_t kQuietNaN = 0x7FC00000u;
 
 // Raw buffer resource over `bytes` bytes at `base` (gfx9-family descriptor word 3: 32-bit data
 // format, no swizzle). Loads outside [0, bytes) return zeros and stores there are dropped, so an
@@ -258,19 +267,14 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
       (uint32_t)lane64 * 2u, 0, 0);
   [[maybe_unused]] double qs = 0.0;
   if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) qs = (double)*a.qscale;
-  // Split rows: this slice's current epoch (the upper half of its exchange word), read now so the
-  // barrier does not wait for it. Every wavefront reads it unconditionally (from gamma, a valid
-  // dummy, when rows are whole): a load under a branch would make the compiler wait for it at the
-  // branch join. Only the 32 bits in use are loaded: with a 64-bit load the compiler reused the
-  // unused half's register at once, and that wait held the first row load back until this
-  // memory-side load had returned.
+  // Split rows: the token's current epoch, read now so the barrier does not wait for it. Every
+  // wavefront reads it unconditionally (from gamma, a valid dummy, when rows are whole): a load
+  // under a branch would make the compiler wait for it at the branch join.
   [[maybe_unused]] uint32_t epoch_prev = 0;
   if constexpr (MODE != MODE_FIN) {
     const uint32_t* ep =
-        a.slices > 1
-            ? (const uint32_t*)((const uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken) +
-                                slice) + 1
-            : (const uint32_t*)a.gamma;
+        a.slices > 1 ? (const uint32_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken + kWsEpochOffset)
+                     : (const uint32_t*)a.gamma;
     epoch_prev = __hip_atomic_load(ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
@@ -423,35 +427,41 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     for (int i = 0; i < n_waves0; ++i)
       tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, part), i));
     if (a.slices > 1) {
-      uint64_t* slot = (uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken);
+      uint8_t* const blk = a.ws + kWsHeader + (size_t)t * kWsPerToken;
+      uint64_t* const slot = (uint64_t*)blk;
       const int S = a.slices;
       const uint32_t epoch = epoch_prev + 1u;
-      const int m = slice + tid * S;              // this slice's slots
-      if (m < kMaxSlices) {
-        const uint64_t v = ((uint64_t)epoch << 32) |
-                           (m == slice ? (uint64_t)__builtin_bit_cast(uint32_t, tot) : 0ull);
-        __hip_atomic_store(slot + m, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
+        const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__builtin_bit_cast(uint32_t, tot);
+        __hip_atomic_store(slot + slice, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      // lane j < S waits for slice j's word of this epoch
+      // lane j < S waits for slice j's word of this epoch; a partial that never arrives counts
+      // as NaN
       uint32_t bits = 0;
       if (tid < S) {
         uint32_t spins = 0;
         while (true) {
+          if (spins >= a.spin_limit) {
+            __hip_atomic_fetch_or((uint32_t*)a.ws, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            bits = kQuietNaN;
+            break;
+          }
           const uint64_t x = __hip_atomic_load(slot + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if ((uint32_t)(x >> 32) == epoch) {
             bits = (uint32_t)x;
             break;
           }
-          if (++spins > kMaxSpins) {
-            __hip_atomic_fetch_or((uint32_t*)a.ws, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
+          ++spins;
           __builtin_amdgcn_s_sleep(1);
         }
       }
       tot = 0.f;
       for (int j = 0; j < S; ++j)                 // slice order: deterministic
         tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)bits, j));
+      // every slice has read the old epoch (each published epoch, which depends on that read)
+      if (slice == 0 && tid == 0)
+        __hip_atomic_store((uint32_t*)(blk + kWsEpochOffset), epoch, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid == 0) row_total = tot;
   }
@@ -575,6 +585,26 @@ static bool use_nontemporal(int64_t T, int64_t H, int K) {
   return T * (int64_t)K * H * 2 >= kNontemporalRowBytes;
 }
 
+// Compute units of each device, queried once per device (hipDeviceAttributeMultiprocessorCount).
+constexpr int kMaxDevices = 64;
+static std::atomic<int> g_cus[kMaxDevices];
+static int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_FIN_ERR_HIP;
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return MOE_FIN_ERR_HIP;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  *cus = n;
+  return MOE_FIN_OK;
+}
+
+// Polls of a split row's exchange word before a slice gives up (moe_finalize_set_wait_limit).
+static std::atomic<uint32_t> g_spin_limit{kMaxSpins};
+
 static int next_pow2(int x) {
   int p = 1;
   while (p < x) p <<= 1;
@@ -599,13 +629,14 @@ static void finish_config(int K, Config* c) {
   c->lds = (size_t)(G - 1) * c->P * c->L * 32;
 }
 
-// Slices per token for the split row modes. A CU keeps only so many vector memory requests in
-// flight, so a whole row per workgroup leaves bandwidth unused when there are fewer tokens than
-// CUs; splitting costs one cross-workgroup exchange (~1 us). Measured on MI355X (forced slice
-// counts, T = 1..256, hidden 1024..16384, top_k 6..22): up to top_k 8 the best slices hold at
-// least 128 slots and give at most one workgroup per CU, min(slots / 128, 256 / T) (hidden 7168:
-// 7 slices at T = 32, 4 at T = 64, 2 at T = 96..128, whole rows from T = 256); with more routes
-// per token, smaller slices of 64 slots and ~224 workgroups, min(slots / 64, 224 / T), win, but
+// Slices per token for the split row modes, for a device of `cus` compute units. A CU keeps only
+// so many vector memory requests in flight, so a whole row per workgroup leaves bandwidth unused
+// when there are fewer tokens than CUs; splitting costs one cross-workgroup exchange (~1 us).
+// Measured on MI355X, 256 CUs (forced slice counts, T = 1..256, hidden 1024..16384, top_k
+// 6..22): up to top_k 8 the best slices hold at least 128 slots and give at most one workgroup
+// per CU, min(slots / 128, CUs / T) (hidden 7168: 7 slices at T = 32, 4 at T = 64, 2 at
+// T = 96..128, whole rows from T = 256); with more routes per token, smaller slices of 64 slots
+// and ~7/8 of a workgroup per CU, min(slots / 64, (7/8) CUs / T), win, but
 // no more than 16 of them (hidden 12288..16384 at T = 1..8: 16 slices beat 24-32 by 0.4-1.2 us,
 // the exchange growing with the slices polled); with four routes or fewer (about five rows of
 // data per token, e.g. a four-rank sum) whole rows win from T = 96 (0.14-0.16 us at T = 96 and
@@ -614,10 +645,10 @@ static void finish_config(int K, Config* c) {
 // the quantized outputs keep the split: their epilogue is arithmetic-bound, and a whole row puts
 // it on one CU (NVFP4 at T = 96..128, hidden 7168 and 16384: 1.1-2.2 us faster split; FP8
 // 0.6-2.1 us, within 0.1 us at hidden 4096). 1 = whole rows (no workspace).
-static int choose_slices(int64_t T, int nv, int K, bool quantized) {
+static int choose_slices(int64_t T, int nv, int K, bool quantized, int cus) {
   if (K <= 4 && T >= 96 && !quantized && (K + 2) * nv * 16 <= (128 << 10)) return 1;
   const int max_by_h = nv / (K > 8 ? 64 : 128);
-  int S = (int)((K > 8 ? 224 : 256) / (T > 0 ? T : 1));
+  int S = (int)((K > 8 ? cus * 7 / 8 : cus) / (T > 0 ? T : 1));
   if (S > max_by_h) S = max_by_h;
   if (K > 8 && S > 16) S = 16;
   if (S > kMaxSlices) S = kMaxSlices;
@@ -831,7 +862,13 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
                     float eps, void* residual_out, void* norm_out, const float* qscale,
                     void* quant_out, void* scale_out, int sf_layout, void* workspace,
                     void* stream, int route_stride = 0) {
-  const int slices = workspace ? choose_slices(c.T, (int)(c.H / 8), c.K, mode != MODE_RMS) : 1;
+  int slices = 1;
+  if (workspace) {
+    int cus = 0;
+    const int rc = device_cus(&cus);
+    if (rc) return rc;
+    slices = choose_slices(c.T, (int)(c.H / 8), c.K, mode != MODE_RMS, cus);
+  }
   Config cfg;
   if (!make_config(mode, c.T, (int)c.H, c.K, slices, &cfg)) return MOE_FIN_ERR_HIDDEN;
   cfg.nontemporal = use_nontemporal(c.T, c.H, c.K);
@@ -858,6 +895,7 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
   p.ws = (uint8_t*)workspace;
   p.route_stride = route_stride;
   p.pad_blocks = pad_blocks;
+  p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   hipStream_t s = (hipStream_t)stream;
   switch (mode) {
     case MODE_RMS: return to_code(dispatch<MODE_RMS>(c.act, p, cfg, s));
@@ -988,7 +1026,13 @@ using namespace mfin;
 
 extern "C" {
 
-int moe_finalize_version(void) { return 201; }
+int moe_finalize_version(void) { return 300; }
+
+int64_t moe_finalize_set_wait_limit(int64_t polls) {
+  const uint32_t v = polls < 0 ? kMaxSpins
+                               : (polls > (int64_t)UINT32_MAX ? UINT32_MAX : (uint32_t)polls);
+  return (int64_t)g_spin_limit.exchange(v);
+}
 
 int moe_finalize_set_cache_policy(int policy) {
   if (policy != MOE_FIN_CACHE_AUTO && policy != MOE_FIN_CACHE_KEEP &&
@@ -1038,14 +1082,21 @@ size_t moe_finalize_workspace_size(int64_t num_tokens, int64_t hidden, int top_k
 // The launch configuration of entry point `entry` (0 = finalize, 1 = RMSNorm, 2 = quantized) for
 // one shape, with the entry point's own shape checks.
 static int entry_config(int entry, int64_t num_tokens, int64_t hidden, int top_k,
-                        bool with_workspace, Config* c) {
+                        bool with_workspace, int num_cus, Config* c) {
   if (entry < 0 || entry > 2) return MOE_FIN_ERR_QUANT_TYPE;
   if (top_k < 1 || top_k > 64) return MOE_FIN_ERR_BAD_TOPK;
   if (hidden <= 0 || hidden % 8 != 0 || (entry > 0 && hidden > 16384)) return MOE_FIN_ERR_HIDDEN;
   if (num_tokens < 0 || num_tokens > INT32_MAX / 2) return MOE_FIN_ERR_BAD_SHAPE;
   const int64_t T = num_tokens > 0 ? num_tokens : 1;
-  const int slices =
-      entry > 0 && with_workspace ? choose_slices(T, (int)(hidden / 8), top_k, entry == 2) : 1;
+  int slices = 1;
+  if (entry > 0 && with_workspace) {
+    int cus = num_cus;
+    if (cus <= 0) {
+      const int rc = device_cus(&cus);
+      if (rc) return rc;
+    }
+    slices = choose_slices(T, (int)(hidden / 8), top_k, entry == 2, cus);
+  }
   if (!make_config(entry == 0 ? MODE_FIN : MODE_RMS, T, (int)hidden, top_k, slices, c))
     return MOE_FIN_ERR_HIDDEN;
   c->nontemporal = use_nontemporal(T, hidden, top_k);
@@ -1056,7 +1107,8 @@ static int entry_config(int entry, int64_t num_tokens, int64_t hidden, int top_k
 int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden, int top_k,
                                   void* stream) {
   Config c;
-  const int rc = entry_config(entry, num_tokens, hidden, top_k, true, &c);
+  // (T = 0 only validates the shape: no slice rule, so no device query)
+  const int rc = entry_config(entry, num_tokens, hidden, top_k, num_tokens > 0, 0, &c);
   if (rc || num_tokens == 0) return rc;
   hipLaunchKernelGGL(launch_floor_kernel, dim3((unsigned)(c.grid_x * num_tokens)), dim3(c.G * c.L),
                      c.lds, (hipStream_t)stream, 0);
@@ -1064,11 +1116,12 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
 }
 
 int moe_finalize_launch_config(int entry, int64_t num_tokens, int64_t hidden, int top_k,
-                               int with_workspace, int64_t* out, int n_out) {
+                               int with_workspace, int num_cus, int64_t* out, int n_out) {
   if (!out) return MOE_FIN_ERR_NULL_POINTER;
   if (n_out < MOE_FIN_LAUNCH_CONFIG_FIELDS) return MOE_FIN_ERR_BAD_SHAPE;
   Config c;
-  const int rc = entry_config(entry, num_tokens, hidden, top_k, with_workspace != 0, &c);
+  const int rc =
+      entry_config(entry, num_tokens, hidden, top_k, with_workspace != 0, num_cus, &c);
   if (rc) return rc;
   out[0] = (int64_t)c.grid_x * num_tokens;
   out[1] = (int64_t)c.G * c.L;

@@ -53,48 +53,108 @@ def to_dev(inp, dev="cuda"):
     return d
 
 
-def report(name, got, ref_vals, act):
+def _ulps(a, b, act):
     fmt = O.FORMATS[act]
-    ud = ulp_distance(O.encode_bits(got, fmt), O.encode_bits(ref_vals, fmt))
+    return ulp_distance(O.encode_bits(a, fmt), O.encode_bits(b, fmt))
+
+
+def report(name, got, ref_vals, act):
+    ud = _ulps(got, ref_vals, act)
     return {"name": name, "max_ulp": int(ud.max()) if ud.size else 0,
             "n_gt1ulp": int((ud > 1).sum()), "n_diff": int((ud > 0).sum()),
             "n": int(ud.size)}
 
 
+def _one_ulp_rule(name, got, want, lo, hi, act):
+    """Within 1 ulp of the oracle's value everywhere except where the float32 window [lo, hi]
+    itself reaches farther than 1 ulp from it (certified cancellation: there a correct float32
+    evaluation may land farther away). Returns the report with the count of such elements."""
+    ud = _ulps(got, want, act)
+    wide = (_ulps(lo, want, act) > 1) | (_ulps(hi, want, act) > 1)
+    narrow_bad = (ud > 1) & ~wide
+    assert not narrow_bad.any(), f"{int(narrow_bad.sum())} {name} elements > 1 ulp where the " \
+                                 f"float32 window is within 1 ulp; first at " \
+                                 f"{np.argwhere(narrow_bad)[0]}"
+    rep = report(name, got, want, act)
+    rep["n_window_wider_than_1ulp"] = int(wide.sum())
+    return rep
+
+
 def check_finalize(got_s: np.ndarray, ref: Ref, act: str):
-    """Finalize values: every element inside the float32 admissible window."""
+    """Finalize values: every element inside the float32 admissible window, and within 1 ulp of
+    the oracle's wherever that window is."""
     bad = outside(got_s, ref.lo, ref.hi)
     assert not bad.any(), f"{int(bad.sum())} finalize elements outside the float32 window; " \
                           f"first at {np.argwhere(bad)[0]}"
-    rep = report("s", got_s, ref.s, act)
-    assert rep["n_gt1ulp"] <= max(2, rep["n"] // 10000), rep
-    return rep
+    return _one_ulp_rule("s", got_s, ref.s, ref.lo, ref.hi, act)
 
 
 def check_residual(got_R: np.ndarray, ref: Ref, residual: np.ndarray, act: str):
     """residual_out = RNE_T(a + residual) for some a in the admissible window of s; RNE_T is
-    monotone, so it lies between the images of the window's ends."""
+    monotone, so it lies between the images of the window's ends. Within 1 ulp of the oracle's
+    wherever that image is."""
     fmt = O.FORMATS[act]
     rlo = O.round_to_format(ref.lo + residual, fmt)
     rhi = O.round_to_format(ref.hi + residual, fmt)
     bad = outside(got_R, rlo, rhi)
     assert not bad.any(), f"{int(bad.sum())} residual_out elements outside the window; " \
                           f"first at {np.argwhere(bad)[0]}"
-    return report("residual_out", got_R, ref.R, act)
+    return _one_ulp_rule("residual_out", got_R, ref.R, rlo, rhi, act)
+
+
+def oracle_norm_of(got_R: np.ndarray, gamma: np.ndarray, eps, act: str) -> np.ndarray:
+    """The oracle's RMSNorm of a given residual_out (R + 0 rounds to R exactly)."""
+    return O.residual_rmsnorm(got_R, np.zeros_like(got_R), gamma, eps, act)[1]
 
 
 def check_norm(got_N: np.ndarray, got_R: np.ndarray, ref: Ref, gamma: np.ndarray, eps, act: str):
-    """norm_out within 1 ulp of the oracle's wherever residual_out matched the oracle; where an
-    element of residual_out took another value of its window, the norm may move by that
-    difference times gamma / rms (plus 1 ulp)."""
-    fmt = O.FORMATS[act]
-    ud = ulp_distance(O.encode_bits(got_N, fmt), O.encode_bits(ref.N, fmt))
-    same_R = got_R == ref.R
-    ok = ud <= 1
-    rms = np.sqrt(np.mean(ref.R * ref.R, axis=-1, keepdims=True) + float(np.float32(eps)))
-    slack = np.abs(got_R - ref.R) * np.abs(gamma) / rms
-    ulp = spacing(np.maximum(np.abs(got_N), np.abs(ref.N)), act)
-    ok_moved = np.abs(got_N - ref.N) <= slack + ulp
-    bad = ~(ok | (~same_R & ok_moved))
-    assert not bad.any(), f"{int(bad.sum())} norm_out elements off; first at {np.argwhere(bad)[0]}"
-    return report("norm_out", got_N, ref.N, act)
+    """norm_out within 1 ulp, everywhere, of the oracle's RMSNorm of the kernel's own
+    residual_out; reported against the primary oracle's norm_out as well."""
+    own = oracle_norm_of(got_R, gamma, eps, act)
+    ud = _ulps(got_N, own, act)
+    assert ud.max(initial=0) <= 1, f"{int((ud > 1).sum())} norm_out elements > 1 ulp from the " \
+                                   f"oracle's norm of the kernel's residual_out; first at " \
+                                   f"{np.argwhere(ud > 1)[0]}"
+    rep = report("norm_out", got_N, ref.N, act)
+    rep["max_ulp_vs_norm_of_own_residual"] = int(ud.max(initial=0))
+    return rep
+
+
+# ---- accuracy records (written to $MFIN_ACCURACY_JSON at the end of a pytest session) ---------
+ACCURACY = []
+
+
+def record_accuracy(config: str, inp, entry: str, rows: str, reps, R=None, N=None, extra=None):
+    """One record per configuration sub-case: the comparison reports (max ulp and counts against
+    the oracle) and, when residual_out / norm_out are given, their mean absolute error against the
+    unrounded FP64 reference beside the rounding floor (the mean error of rounding that exact
+    result to the activation dtype once) and the oracle's own error ([FI6631] Description and
+    benchmark script: mean |err| of residual_out and norm_out against FP64)."""
+    rec = {"config": config, "T": inp.T, "H": inp.H, "K": inp.K, "act": inp.act_dtype,
+           "scales": inp.scale_dtype, "shared": inp.shared is not None, "seed": inp.seed,
+           "entry": entry, "rows": rows, "checks": reps}
+    if R is not None:
+        res_ref, norm_ref = O.reference_unrounded(np64(inp.rows), inp.idx.numpy(),
+                                                  np64(inp.scales), np64(inp.shared), inp.rsf,
+                                                  np64(inp.residual), np64(inp.gamma), inp.eps)
+        fmt = O.FORMATS[inp.act_dtype]
+        ref = oracle_ref(inp)
+        for name, got, exact, orc in (("residual_out", R, res_ref, ref.R),
+                                      ("norm_out", N, norm_ref, ref.N)):
+            if got is None:
+                continue
+            rec[name] = {"mean_abs_err": float(np.abs(got - exact).mean()),
+                         "oracle_mean_abs_err": float(np.abs(orc - exact).mean()),
+                         "floor_mean_abs_err": float(np.abs(O.round_to_format(exact, fmt)
+                                                            - exact).mean()),
+                         "max_abs_err": float(np.abs(got - exact).max())}
+    if extra:
+        rec.update(extra)
+    ACCURACY.append(rec)
+    return rec
+
+
+def write_accuracy(path: str, command: str) -> None:
+    import json
+    with open(path, "w") as fh:
+        json.dump({"command": command, "records": ACCURACY}, fh, indent=1)

@@ -115,7 +115,7 @@ def test_rmsnorm_validation_codes():
     assert rms(res_out=D) == -9                # residual_out overlaps norm_out
     assert rms(T=0) == 0
     need = M.moe_finalize_workspace_size(4, 1024, 8)
-    assert need == 256 + 4 * 512
+    assert need == 256 + 4 * 256
     assert rms(ws=WS + 64, ws_bytes=need) == -5           # workspace must be 256-byte aligned
     assert rms(ws=WS, ws_bytes=need - 1) == -11           # too small
     assert rms(ws=E, ws_bytes=need) == -9                 # overlaps residual
@@ -223,16 +223,35 @@ def test_launch_config_validation_codes():
                        ((1, 4, 1004, 8), M.MoeFinalizeError), ((1, 4, 16392, 8), M.MoeFinalizeError),
                        ((1, -1, 1024, 8), M.MoeFinalizeError)]:
         with pytest.raises(code):
-            cfg(*args)
+            cfg(*args, num_cus=256)
     L = M.LIB
     out = (ctypes.c_int64 * 9)()
-    assert L.moe_finalize_launch_config(1, 4, 1024, 8, 1, None, 9) == -1
-    assert L.moe_finalize_launch_config(1, 4, 1024, 8, 1, out, 8) == -2
-    assert L.moe_finalize_launch_config(3, 4, 1024, 8, 1, out, 9) == -7
-    assert L.moe_finalize_launch_config(1, 4, 1024, 65, 1, out, 9) == -3
-    assert L.moe_finalize_launch_config(1, 4, 16392, 8, 1, out, 9) == -4
-    assert L.moe_finalize_launch_config(0, 4, 16392, 8, 0, out, 9) == 0   # finalize: any hidden
-    assert cfg(1, 0, 7168, 8)["workgroups"] == 0
+    assert L.moe_finalize_launch_config(1, 4, 1024, 8, 1, 256, None, 9) == -1
+    assert L.moe_finalize_launch_config(1, 4, 1024, 8, 1, 256, out, 8) == -2
+    assert L.moe_finalize_launch_config(3, 4, 1024, 8, 1, 256, out, 9) == -7
+    assert L.moe_finalize_launch_config(1, 4, 1024, 65, 1, 256, out, 9) == -3
+    assert L.moe_finalize_launch_config(1, 4, 16392, 8, 1, 256, out, 9) == -4
+    assert L.moe_finalize_launch_config(0, 4, 16392, 8, 0, 256, out, 9) == 0   # finalize: any hidden
+    assert cfg(1, 0, 7168, 8, num_cus=256)["workgroups"] == 0
+    # the device's own count is only needed (and queried) for a split-row configuration
+    assert L.moe_finalize_launch_config(0, 4, 1024, 8, 1, 0, out, 9) == 0
+    assert L.moe_finalize_launch_config(1, 4, 1024, 8, 0, 0, out, 9) == 0
+
+
+def test_slice_rule_follows_the_cu_count():
+    """The slice rule scales with the device's compute units (injected here): at most one
+    workgroup per CU up to top_k 8, about 7/8 of one above, within the hidden-size bounds."""
+    cfg = M.moe_finalize_launch_config
+    # hidden 7168, top_k 8, T = 64: min(896 / 128, CUs / 64) slices
+    assert [cfg(1, 64, 7168, 8, num_cus=c)["slices"] for c in (64, 128, 256, 304, 512)] == \
+        [1, 2, 4, 4, 7]
+    # T = 128: two slices on 256 CUs, whole rows on 128
+    assert cfg(1, 128, 7168, 8, num_cus=256)["slices"] == 2
+    assert cfg(1, 128, 7168, 8, num_cus=128)["slices"] == 1
+    # top_k 22, hidden 2048, T = 16: min(256 / 64, 7/8 CUs / 16)
+    assert [cfg(1, 16, 2048, 22, num_cus=c)["slices"] for c in (32, 64, 256)] == [1, 3, 4]
+    # the quantized entry splits by the same counts
+    assert cfg(2, 64, 6144, 8, num_cus=128)["slices"] == 2
 
 
 def test_launch_config_every_shape_has_a_kernel():
@@ -240,8 +259,9 @@ def test_launch_config_every_shape_has_a_kernel():
     entry kind, with and without a workspace): the chosen configuration has a compiled kernel, fits
     one workgroup (whole wavefronts, <= 1024 lanes, <= 64 KiB LDS), gives every route group work,
     covers each token's 8-element slots with non-empty slices, splits rows only within the slice
-    rule's bounds (<= 64; up to top_k 8 <= hidden/1024 slices and <= 256/T, above it <= hidden/512,
-    <= 224/T and <= 16; whole rows for plain RMSNorm with top_k <= 4 from T = 96 while a token's
+    rule's bounds for a device of C compute units (<= 16; up to top_k 8 <= hidden/1024 slices and
+    <= C/T, above it <= hidden/512 and <= (7/8)C/T; whole rows for plain RMSNorm with top_k <= 4
+    from T = 96 while a token's
     data stays within 128 KiB, and without a workspace), sizes whole-row
     workgroups by the slot rule (four-wavefront multiples from T = 1024 while a route group has at
     most 8 routes), and streams nontemporally exactly from 4 MiB of rows."""
@@ -251,13 +271,14 @@ def test_launch_config_every_shape_has_a_kernel():
           12288, 16376, 16384]
     Ks = [1, 2, 3, 4, 5, 6, 8, 10, 16, 17, 22, 31, 32, 33, 63, 64]
     n = 0
-    for entry in (0, 1, 2):
-        for ws in (False, True):
+    for cus, entry, ws in [(256, e, w) for e in (0, 1, 2) for w in (False, True)] + \
+            [(c, e, True) for c in (80, 304) for e in (1, 2)]:
+        if True:
             for T in Ts:
                 for H in Hs:
                     nv = H // 8
                     for K in Ks:
-                        c = M.moe_finalize_launch_config(entry, T, H, K, ws)
+                        c = M.moe_finalize_launch_config(entry, T, H, K, ws, num_cus=cus)
                         n += 1
                         where = (entry, ws, T, H, K, c)
                         G, P, span = c["route_groups"], c["slots_per_lane"], c["slot_span"]
@@ -276,10 +297,11 @@ def test_launch_config_every_shape_has_a_kernel():
                             continue
                         S = c["slices"]
                         assert c["workgroups"] == T * S, where
-                        bound = min(nv // 64, 224 // T, 16) if K > 8 else min(nv // 128, 256 // T)
+                        bound = (min(nv // 64, cus * 7 // 8 // T, 16) if K > 8
+                                 else min(nv // 128, cus // T))
                         if K <= 4 and T >= 96 and entry == 1 and (K + 2) * nv * 16 <= 128 << 10:
                             bound = 1
-                        assert 1 <= S <= max(1, min(bound, 64)), where
+                        assert 1 <= S <= max(1, min(bound, 16)), where
                         if not ws:
                             assert S == 1, where
                         assert (S - 1) * span < nv <= S * span, where
@@ -294,7 +316,7 @@ def test_launch_config_every_shape_has_a_kernel():
                             r = 256 if quad else 64
                             assert lanes_per_group == -(-per_lane // r) * r, where
                             assert span == lanes_per_group * P, where
-    assert n == 3 * 2 * len(Ts) * len(Hs) * len(Ks)
+    assert n == (3 * 2 + 2 * 2) * len(Ts) * len(Hs) * len(Ks)
 
 
 def test_cache_policy_setting():
@@ -304,20 +326,20 @@ def test_cache_policy_setting():
     assert L.moe_finalize_set_cache_policy(M.MOE_FIN_CACHE_AUTO) == M.MOE_FIN_CACHE_AUTO
     try:
         big, small = (1, 128, 7168, 8), (1, 16, 6144, 8)
-        assert M.moe_finalize_launch_config(*big)["nontemporal"] == 1
-        assert M.moe_finalize_launch_config(*small)["nontemporal"] == 0
+        assert M.moe_finalize_launch_config(*big, num_cus=256)["nontemporal"] == 1
+        assert M.moe_finalize_launch_config(*small, num_cus=256)["nontemporal"] == 0
         assert M.moe_finalize_set_cache_policy(M.MOE_FIN_CACHE_KEEP) == M.MOE_FIN_CACHE_AUTO
         for e in (0, 1, 2):
-            assert M.moe_finalize_launch_config(e, 128, 7168, 8)["nontemporal"] == 0
+            assert M.moe_finalize_launch_config(e, 128, 7168, 8, num_cus=256)["nontemporal"] == 0
         assert L.moe_finalize_set_cache_policy(3) == -12 and L.moe_finalize_set_cache_policy(-1) == -12
         with pytest.raises(M.MoeFinalizeError):
             M.moe_finalize_set_cache_policy(7)
         assert M.moe_finalize_set_cache_policy(M.MOE_FIN_CACHE_STREAM) == M.MOE_FIN_CACHE_KEEP
         for e in (0, 1, 2):
-            assert M.moe_finalize_launch_config(e, 1, 1024, 1)["nontemporal"] == 1
+            assert M.moe_finalize_launch_config(e, 1, 1024, 1, num_cus=256)["nontemporal"] == 1
     finally:
         M.moe_finalize_set_cache_policy(M.MOE_FIN_CACHE_AUTO)
-    assert M.moe_finalize_launch_config(*small)["nontemporal"] == 0
+    assert M.moe_finalize_launch_config(*small, num_cus=256)["nontemporal"] == 0
 
 
 def test_binding_rejects_mismatched_tensors():

@@ -22,7 +22,7 @@ import oracle as O  # noqa: E402
 from synth import MoeInputs, make_inputs, make_inputs_on_device, workload_seed  # noqa: E402
 from tests.comparators import ulp_distance  # noqa: E402
 from tests.parity import (bits16, check_finalize, check_norm, check_residual,  # noqa: E402
-                          np64, oracle_ref, to_dev)
+                          np64, oracle_ref, record_accuracy, to_dev)
 
 ACT_T = {"bf16": torch.bfloat16, "fp16": torch.float16}
 
@@ -71,7 +71,9 @@ def run_rmsnorm(inp, d=None, residual_out=True, use_ws=True):
     return ro, no
 
 
-def full_check(inp, *, finalize=True, rmsnorm=True):
+def full_check(inp, *, finalize=True, rmsnorm=True, config=None):
+    """Finalize and RMSNorm (split and whole rows) against the oracle; with `config`, one
+    accuracy record per entry point and row mode."""
     _say(f"case T={inp.T} H={inp.H} K={inp.K} act={inp.act_dtype} scales={inp.scale_dtype} "
          f"seed={inp.seed} shared={inp.shared is not None}")
     ref = oracle_ref(inp, with_norm=rmsnorm)
@@ -79,20 +81,24 @@ def full_check(inp, *, finalize=True, rmsnorm=True):
     d = to_dev(inp)
     if finalize:
         s = run_finalize(inp, d)
-        reps.append(check_finalize(np64(s), ref, inp.act_dtype))
+        r = check_finalize(np64(s), ref, inp.act_dtype)
+        reps.append(r)
+        if config:
+            record_accuracy(config, inp, "moe_finalize_run", "-", [r])
     if rmsnorm:
         for use_ws in (True, False):      # split rows (workspace) and whole-row workgroups
             ro, no = run_rmsnorm(inp, d, use_ws=use_ws)
             R, N = np64(ro), np64(no)
-            reps.append(check_residual(R, ref, np64(inp.residual), inp.act_dtype))
-            reps.append(check_norm(N, R, ref, np64(inp.gamma), inp.eps, inp.act_dtype))
-        # mean absolute error vs the unrounded FP64 reference, as the pages report it
-        ref_res, ref_norm = O.reference_unrounded(np64(inp.rows), inp.idx.numpy(),
-                                                  np64(inp.scales), np64(inp.shared), inp.rsf,
-                                                  np64(inp.residual), np64(inp.gamma), inp.eps)
-        _say(f"  mean|err| residual_out {np.abs(R - ref_res).mean():.3e} "
-             f"(floor {np.abs(ref.R - ref_res).mean():.3e}), norm_out "
-             f"{np.abs(N - ref_norm).mean():.3e}")
+            pair = [check_residual(R, ref, np64(inp.residual), inp.act_dtype),
+                    check_norm(N, R, ref, np64(inp.gamma), inp.eps, inp.act_dtype)]
+            reps += pair
+            if config:
+                rec = record_accuracy(config, inp, "moe_finalize_rmsnorm_run",
+                                      "split" if use_ws else "whole", pair, R, N)
+                _say(f"  mean|err| residual_out {rec['residual_out']['mean_abs_err']:.3e} "
+                     f"(floor {rec['residual_out']['floor_mean_abs_err']:.3e}), norm_out "
+                     f"{rec['norm_out']['mean_abs_err']:.3e} "
+                     f"(floor {rec['norm_out']['floor_mean_abs_err']:.3e})")
     for r in reps:
         _say("  ", r)
     return reps
@@ -100,18 +106,19 @@ def full_check(inp, *, finalize=True, rmsnorm=True):
 
 # ---- the workloads -------------------------------------------------------------------------------
 def test_tiny_t4_h1024_k8():
-    full_check(make_inputs(4, 1024, 8, seed=workload_seed("tiny", 4)))
+    full_check(make_inputs(4, 1024, 8, seed=workload_seed("tiny", 4)), config="tiny")
 
 
 @pytest.mark.parametrize("T", [1, 4, 16])
 def test_decode_h6144_k8(T):
-    full_check(make_inputs(T, 6144, 8, seed=workload_seed("decode", T)))
+    full_check(make_inputs(T, 6144, 8, seed=workload_seed("decode", T)), config="decode")
 
 
 @pytest.mark.parametrize("act", ["bf16", "fp16"])
 @pytest.mark.parametrize("T", [32, 64, 128])
 def test_larger_decode_h7168_k8(T, act):
-    full_check(make_inputs(T, 7168, 8, act_dtype=act, seed=workload_seed("larger", T, act)))
+    full_check(make_inputs(T, 7168, 8, act_dtype=act, seed=workload_seed("larger", T, act)),
+               config="larger")
 
 
 @pytest.mark.parametrize("HK", [(2048, 22), (3584, 16), (2048, 6), (2048, 10)])
@@ -120,7 +127,7 @@ def test_larger_decode_h7168_k8(T, act):
 def test_high_topk(T, sdt, HK):
     H, K = HK
     full_check(make_inputs(T, H, K, scale_dtype=sdt, with_shared=False,
-                           seed=workload_seed("highk", T, "bf16", sdt, K)))
+                           seed=workload_seed("highk", T, "bf16", sdt, K)), config="high_topk")
 
 
 # ---- exactness: indices, route selection, poison -------------------------------------------------
@@ -402,8 +409,8 @@ def test_nvfp4(TH, layout):
     for use_ws in (True, False):
         ro, no, qo, so = run_quant(inp, M.MOE_QUANT_NVFP4, gs, layout, use_ws=use_ws)
         R, N = np64(ro), np64(no)
-        check_residual(R, ref, np64(inp.residual), "bf16")
-        check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")
+        pair = [check_residual(R, ref, np64(inp.residual), "bf16"),
+                check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")]
         nb = H // 16
         same_blk = (N == ref.N).reshape(T, nb, 16).all(-1)
         c_g = qo.reshape(T, nb, 8)
@@ -417,6 +424,11 @@ def test_nvfp4(TH, layout):
         assert np.array_equal(c_g[same_blk], c_o[same_blk])
         assert np.array_equal(sf_g[same_blk], sf_o[same_blk])
         assert same_blk.mean() > 0.98, same_blk.mean()
+        if (T, H) == (64, 6144):
+            record_accuracy("quant", inp, f"moe_finalize_quant_run NVFP4 layout={layout}",
+                            "split" if use_ws else "whole", pair, R, N,
+                            {"codes_and_scales_bit_exact_vs_quant_of_own_norm_out": True,
+                             "blocks_equal_to_oracle_norm_out": float(same_blk.mean())})
         # blocks within one ulp of it: scale within one E4M3 step
         near_blk = ~same_blk & (ulp_distance(O.encode_bits(N, O.FORMATS["bf16"]),
                                              O.encode_bits(ref.N, O.FORMATS["bf16"]))
@@ -445,7 +457,8 @@ def test_fp8(T, H):
     for use_ws in (True, False):
         ro, no, qo, _ = run_quant(inp, M.MOE_QUANT_FP8_E4M3, s8, use_ws=use_ws)
         R, N = np64(ro), np64(no)
-        check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")
+        pair = [check_residual(R, ref, np64(inp.residual), "bf16"),
+                check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")]
         # the codes are the FP8 quantization of the kernel's own rounded norm_out, bit for bit
         assert np.array_equal(qo, O.quant_fp8(N, s8))
         same = N == ref.N
@@ -457,6 +470,11 @@ def test_fp8(T, H):
         d = np.abs((qo[near] & 0x7F).astype(int) - (codes_or[near] & 0x7F).astype(int))
         assert d.max(initial=0) <= 1
         assert same.mean() > 0.99
+        if (T, H) == (64, 6144):
+            record_accuracy("quant", inp, "moe_finalize_quant_run FP8",
+                            "split" if use_ws else "whole", pair, R, N,
+                            {"codes_bit_exact_vs_quant_of_own_norm_out": True,
+                             "elements_equal_to_oracle_norm_out": float(same.mean())})
 
 
 def test_quant_codec_edges():
@@ -928,37 +946,92 @@ def test_outputs_stay_in_bounds_and_inputs_untouched(THK):
         assert torch.equal(d[k], v), k
 
 
-def test_split_row_timeout_is_flagged_and_bounded():
-    """Failure detection of the split-row exchange, forced from the host: one token's workspace
-    slots are set so that its two slices expect different epochs and can never agree. Each slice
-    gives up after the kernel's own bounded wait, sets the sticky flag in the workspace header and
-    exits; the call completes. A zero-filled workspace then works again."""
-    import time
+def test_split_row_timeout_is_flagged_poisoned_and_bounded():
+    """Failure detection of the split-row exchange, forced from the host: with a wait limit of 0
+    polls every slice of a split row gives up at once, without waiting. Each sets the sticky flag
+    in the workspace header and counts the partials it did not see as NaN, so norm_out and the
+    quantized outputs come out NaN (FP8 code 0x7F; NVFP4 block scale 0x7F, codes 0) while
+    residual_out is still exact; every call completes. With the default limit and a re-zeroed
+    workspace the next call is correct again."""
     inp = make_inputs(1, 2048, 8, seed=800)          # T=1, hidden 2048: two slices per row
     assert M.moe_finalize_launch_config(1, 1, 2048, 8)["slices"] == 2
+    assert M.moe_finalize_launch_config(2, 1, 2048, 8)["slices"] == 2
     d = to_dev(inp)
-    need = M.moe_finalize_workspace_size(1, 2048, 8)
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
-    slots = ws[256:256 + 512].view(torch.int64)
-    slots[0::2] = 5 << 32                             # slice 0 will wait for epoch 6 ...
-    slots[1::2] = 9 << 32                             # ... slice 1 for epoch 10
+    ref = oracle_ref(inp)
+    ws = torch.zeros(M.moe_finalize_workspace_size(1, 2048, 8), dtype=torch.uint8, device="cuda")
     ro = torch.empty(1, 2048, dtype=torch.bfloat16, device="cuda")
     no = torch.empty_like(ro)
-    _say("forcing a split-row timeout (bounded wait, a few seconds)")
-    t0 = time.time()
-    M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
-                               d["residual"], d["gamma"], inp.eps, ro, no, ws)
-    torch.cuda.synchronize()
-    _say(f"  returned after {time.time() - t0:.2f} s")
-    assert int(ws[:4].view(torch.int32).item()) == 1
+    q8 = torch.zeros(1, 2048, dtype=torch.uint8, device="cuda")
+    q4 = torch.full((1, 1024), 0xAB, dtype=torch.uint8, device="cuda")
+    lay = M.MOE_SF_SWIZZLED_128x4
+    sf = torch.full((M.moe_finalize_sf_size(1, 2048, lay),), 0xCD, dtype=torch.uint8,
+                    device="cuda")
+    qs = torch.tensor([100.0], dtype=torch.float32, device="cuda")
+    _say("forcing split-row timeouts with a wait limit of 0 polls")
+    prev = M.moe_finalize_set_wait_limit(0)
+    try:
+        assert prev == 1 << 22
+        M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                   d["residual"], d["gamma"], inp.eps, ro, no, ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 1
+        check_residual(np64(ro), ref, np64(inp.residual), "bf16")
+        assert torch.isnan(no.float()).all()
+        ro2 = torch.empty_like(ro)
+        M.moe_finalize_quant_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                 d["residual"], d["gamma"], inp.eps, M.MOE_QUANT_FP8_E4M3, qs,
+                                 q8, None, 0, ro2, None, ws)
+        M.moe_finalize_quant_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
+                                 d["residual"], d["gamma"], inp.eps, M.MOE_QUANT_NVFP4, qs, q4,
+                                 sf, lay, None, None, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(ro2, ro)
+        assert (q8 == 0x7F).all()
+        assert (q4 == 0).all()
+        offs = _sf_offsets(1, 2048, lay).ravel()
+        sfh = sf.cpu().numpy()
+        assert (sfh[offs] == 0x7F).all()
+        pad = np.ones(sfh.size, bool)
+        pad[offs] = False
+        assert not sfh[pad].any()
+    finally:
+        assert M.moe_finalize_set_wait_limit(-1) == 0
+    assert M.moe_finalize_set_wait_limit(-1) == 1 << 22
     ws.zero_()
-    ref = oracle_ref(inp)
     M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
                                d["residual"], d["gamma"], inp.eps, ro, no, ws)
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32).item()) == 0
     check_residual(np64(ro), ref, np64(inp.residual), "bf16")
     check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, "bf16")
+
+
+def test_split_row_epochs_are_per_token():
+    """The exchange words of a split row: after calls with different slice counts on one
+    workspace, each token's epoch word counts the split calls that touched the token, and its
+    slots 0..S-1 carry that epoch (the slots past S of the last call hold older epochs)."""
+    ws = workspace(64)
+    ws.zero_()
+    seq = [(1, 2048, 8), (4, 7168, 8), (1, 6144, 8), (64, 7168, 8), (1, 2048, 8)]
+    count = {}
+    last_s = {}
+    for T, H, K in seq:
+        inp = make_inputs(T, H, K, seed=810 + T + H)
+        S = M.moe_finalize_launch_config(1, T, H, K)["slices"]
+        assert S > 1
+        ro, no = run_rmsnorm(inp)
+        ref = oracle_ref(inp)
+        check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, "bf16")
+        for t in range(T):
+            count[t] = count.get(t, 0) + 1
+            last_s[t] = S
+    blocks = ws[256:256 + 64 * 256].view(64, 256).cpu()
+    for t, n in count.items():
+        epoch = int(blocks[t, 128:132].view(torch.int32).item())
+        assert epoch == n, (t, epoch, n)
+        slot_epochs = (blocks[t, :128].view(torch.int64) >> 32).numpy()
+        assert (slot_epochs[:last_s[t]] == n).all(), (t, slot_epochs)
+        assert (slot_epochs[last_s[t]:] < n).all(), (t, slot_epochs)
 
 
 # ---- one GPU's share of the cross-rank reduction (moe_rank_sum_*_run) -----------------------------
