@@ -56,7 +56,8 @@
  *     slices of its row; it stays 0 in normal use. A workgroup that gives up counts the missing
  *     partial sums as NaN, so its part of that token's norm_out is NaN (FP8 codes 0x7F; NVFP4
  *     block scales 0x7F with zero codes) instead of a wrong finite value; residual_out is not
- *     affected. After the flag is set, zero the workspace again before its next use.
+ *     affected. No reset is needed afterwards (a late workgroup still finds its row's partials,
+ *     and the next call works normally); the flag stays set until the caller clears it.
  *     Progress: a token's slices are consecutive workgroups and rows are split only while the
  *     grid stays near one workgroup per compute unit of the current device (its count is
  *     queried once per device), so workgroups dispatched before a waiting one never wait on it

@@ -74,22 +74,26 @@ struct Params {
 // Split rows. When a token's row is spread over `slices` workgroups, each workgroup publishes
 // the sum of squares of its slice in the caller's workspace and waits for the other slices of
 // its token. Layout: a 256-byte header whose first word is a sticky timeout flag, then one
-// 256-byte block per token: kMaxSlices 64-bit slots (bytes 0..127, one cache line) and the
-// token's 32-bit epoch word (byte 128, a line of its own). A slot carries (epoch << 32 | float
-// bits of a partial) in ONE relaxed device-scope atomic word, so the flag and the data become
-// visible together and no release/acquire fences (L2 writeback / invalidate) are needed. Every
-// slice of a call reads the token's epoch E at its start, publishes E + 1 in its own slot and
-// waits until slots 0..slices-1 carry E + 1; after its wait, slice 0 stores E + 1 as the token's
-// epoch. That store comes after every slice has read E (each published E + 1, which depends on
-// its read), and the next call on the stream starts after this one ends, so each call sees the
-// epoch the previous one left. A slot holds at most the token's current epoch between calls, so
-// stale slots of a call with more slices never match. A zero-filled workspace is valid, no call
-// needs a reset, the slice count may change from call to call, and a call writes only the slots
-// it uses and one epoch word per token. When a slice gives up waiting (spin_limit polls), it
-// sets the header flag and counts the missing partials as NaN, so its part of norm_out (and of
-// the quantized outputs) is NaN rather than a wrong finite value; residual_out is unaffected.
+// 256-byte block per token: kMaxSlices 64-bit slots (bytes 0..127, one cache line), then the
+// token's 32-bit epoch word and 32-bit arrival count (bytes 128 and 132, a line of their own).
+// A slot carries (epoch << 32 | float bits of a partial) in ONE relaxed device-scope atomic word,
+// so the flag and the data become visible together and no release/acquire fences (L2 writeback /
+// invalidate) are needed. Every slice of a call reads the token's epoch E at its start,
+// publishes E + 1 in its own slot, adds itself to the arrival count, and waits until slots
+// 0..slices-1 carry E + 1. The slice whose addition completes the count (all slices have read E
+// by then: each added itself after publishing E + 1, which depends on its read) resets the count
+// and stores E + 1 as the token's epoch; the next call on the stream starts after this one ends
+// and sees it. So the epoch advances exactly when every slice of the call has read it, even when
+// a slice runs late: a late slice still reads E, finds the others' E + 1 and completes. A slot
+// holds at most the token's current epoch between calls, so stale slots of a call with more
+// slices never match. A zero-filled workspace is valid, no call needs a reset (also after a
+// timeout), the slice count may change from call to call, and a call writes only the slots it
+// uses and one line of epoch and count per token. When a slice gives up waiting (spin_limit
+// polls), it sets the header flag and counts the missing partials as NaN, so its part of
+// norm_out (and of the quantized outputs) is NaN rather than a wrong finite value; residual_out
+// is unaffected.
 constexpr int kMaxSlices = 16;
-constexpr size_t kWsHeader = 256, kWsPerToken = 256, kWsEpochOffset = 128;
+constexpr size_t kWsHeader = 256, kWsPerToken = 256, kWsEpochOffset = 128, kWsCountOffset = 132;
 constexpr uint32_t kMaxSpins = 1u << 22;      // ~0.1-0.5 s of polling, then give up (flagged)
 constexpr uint32_t kQuietNaN = 0x7FC00000u;
 
@@ -431,9 +435,12 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
       uint64_t* const slot = (uint64_t*)blk;
       const int S = a.slices;
       const uint32_t epoch = epoch_prev + 1u;
+      uint32_t arrived = 0;
       if (tid == 0) {
         const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__builtin_bit_cast(uint32_t, tot);
         __hip_atomic_store(slot + slice, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        arrived = __hip_atomic_fetch_add((uint32_t*)(blk + kWsCountOffset), 1u, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
       }
       // lane j < S waits for slice j's word of this epoch; a partial that never arrives counts
       // as NaN
@@ -458,10 +465,13 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
       tot = 0.f;
       for (int j = 0; j < S; ++j)                 // slice order: deterministic
         tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)bits, j));
-      // every slice has read the old epoch (each published epoch, which depends on that read)
-      if (slice == 0 && tid == 0)
+      // the last slice to arrive: every slice has read the old epoch
+      if (tid == 0 && arrived == (uint32_t)(S - 1)) {
+        __hip_atomic_store((uint32_t*)(blk + kWsCountOffset), 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store((uint32_t*)(blk + kWsEpochOffset), epoch, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     if (tid == 0) row_total = tot;
   }
