@@ -90,6 +90,7 @@ extern "C" {
 #define MOE_FIN_ERR_HIP (-10)           /* the HIP runtime refused the launch               */
 #define MOE_FIN_ERR_WORKSPACE (-11)     /* workspace smaller than moe_finalize_workspace_size */
 #define MOE_FIN_ERR_POLICY (-12)        /* unknown cache policy                             */
+#define MOE_FIN_ERR_SCRATCH (-13)       /* num_tokens above the static scratch's 1024       */
 
 /* Element types. */
 #define MOE_DTYPE_BF16 0
@@ -146,6 +147,31 @@ int moe_finalize_rmsnorm_run(const void* permuted_rows, int64_t num_permuted_row
                              void* workspace, size_t workspace_bytes,
                              int64_t num_tokens, int64_t hidden, int top_k, int act_dtype,
                              void* stream);
+
+/*
+ * moe_finalize_rmsnorm_noalloc_run -- moe_finalize_rmsnorm_run for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, kernels and results, with no workspace argument. It calls
+ * no allocating routine; the split-row exchange uses a static scratch array inside the library,
+ * 262,400 bytes per device (256 + 256 per token for up to 1024 tokens), which each GPU the
+ * library runs on holds until the process ends. The first call on a device also enqueues, ahead
+ * of its own work on `stream`, one small kernel that zeroes that device's scratch.
+ *   num_tokens  0..1024; more gives MOE_FIN_ERR_SCRATCH (nothing is enqueued).
+ * All calls on one device share its scratch, which keeps the last call's exchange words: calls
+ * that may overlap on one device (different streams, or threads) race and must not be made;
+ * calls in order on one stream need no reset, and a timed-out call needs none either (see
+ * "Workspace"). The timeout flag lives in the scratch and is not readable by the caller; a
+ * timed-out call still shows as NaN norm_out. Other arguments, errors and results exactly as
+ * moe_finalize_rmsnorm_run with a workspace (bit-identical outputs).
+ */
+int moe_finalize_rmsnorm_noalloc_run(const void* permuted_rows, int64_t num_permuted_rows,
+                                     const int32_t* expanded_idx_to_permuted_idx,
+                                     const void* expert_scales, int scales_dtype,
+                                     const void* shared_expert_output,
+                                     float routed_scaling_factor, const void* residual,
+                                     const void* gamma, float eps, void* residual_out,
+                                     void* norm_out, int64_t num_tokens, int64_t hidden,
+                                     int top_k, int act_dtype, void* stream);
 
 /*
  * moe_finalize_quant_run -- moe_finalize_rmsnorm_run followed by quantization of norm

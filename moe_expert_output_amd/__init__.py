@@ -9,7 +9,8 @@ from .binding import (  # noqa: F401
     MOE_FIN_CACHE_AUTO, MOE_FIN_CACHE_KEEP, MOE_FIN_CACHE_STREAM, MOE_QUANT_FP8_E4M3,
     MOE_QUANT_NVFP4, MOE_SF_LINEAR, MOE_SF_SWIZZLED_128x4, MoeFinalizeError,
     moe_finalize_error_string, moe_finalize_launch_config, moe_finalize_launch_floor_run,
-    moe_finalize_quant_run, moe_finalize_rmsnorm_run, moe_finalize_run,
+    moe_finalize_quant_run, moe_finalize_rmsnorm_noalloc_run, moe_finalize_rmsnorm_run,
+    moe_finalize_run,
     moe_finalize_set_cache_policy, moe_finalize_set_wait_limit, moe_finalize_sf_size,
     moe_finalize_stream_floor_run, moe_finalize_version, moe_finalize_workspace_size,
     moe_quantize_run, moe_rank_sum_quant_run, moe_rank_sum_rmsnorm_run, moe_residual_rmsnorm_run,

@@ -26,7 +26,8 @@ EXPORTED = ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_
             "moe_finalize_launch_floor_run", "moe_finalize_workspace_size", "moe_quantize_run",
             "moe_residual_rmsnorm_run", "moe_finalize_stream_floor_run",
             "moe_rank_sum_rmsnorm_run", "moe_rank_sum_quant_run", "moe_finalize_launch_config",
-            "moe_finalize_set_cache_policy", "moe_finalize_set_wait_limit")
+            "moe_finalize_set_cache_policy", "moe_finalize_set_wait_limit",
+            "moe_finalize_rmsnorm_noalloc_run")
 
 _ACT = {torch.bfloat16: MOE_DTYPE_BF16, torch.float16: MOE_DTYPE_FP16}
 _SCALE = {torch.float32: MOE_DTYPE_FP32, torch.bfloat16: MOE_DTYPE_BF16}
@@ -49,6 +50,9 @@ def _load() -> ctypes.CDLL:
     sz = ctypes.c_size_t
     lib.moe_finalize_rmsnorm_run.argtypes = [vp, i64, vp, vp, i32, vp, f32, vp, vp, f32, vp, vp,
                                              vp, sz, i64, i64, i32, i32, vp]
+    lib.moe_finalize_rmsnorm_noalloc_run.argtypes = [vp, i64, vp, vp, i32, vp, f32, vp, vp, f32,
+                                                     vp, vp, i64, i64, i32, i32, vp]
+    lib.moe_finalize_rmsnorm_noalloc_run.restype = ctypes.c_int
     lib.moe_finalize_quant_run.argtypes = [vp, i64, vp, vp, i32, vp, f32, vp, vp, f32, i32, vp,
                                            vp, vp, i32, vp, vp, vp, sz, i64, i64, i32, i32, vp]
     lib.moe_quantize_run.argtypes = [vp, i64, i64, i32, i32, vp, vp, vp, i32, vp]
@@ -282,6 +286,25 @@ def moe_finalize_rmsnorm_run(permuted_rows: torch.Tensor,
         _ptr(permuted_rows), permuted_rows.shape[0], _ptr(expanded_idx_to_permuted_idx),
         _ptr(expert_scales), sdt, _ptr(shared_expert_output), float(routed_scaling_factor),
         _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out), _ptr(norm_out), wp, wb,
+        T, H, K, act, _stream(residual, stream)))
+
+
+def moe_finalize_rmsnorm_noalloc_run(permuted_rows: torch.Tensor,
+                                     expanded_idx_to_permuted_idx: torch.Tensor,
+                                     expert_scales: Optional[torch.Tensor],
+                                     shared_expert_output: Optional[torch.Tensor],
+                                     routed_scaling_factor: float, residual: torch.Tensor,
+                                     gamma: torch.Tensor, eps: float,
+                                     residual_out: Optional[torch.Tensor], norm_out: torch.Tensor,
+                                     stream=None) -> None:
+    H = residual.shape[-1]
+    act, sdt, T, K = _common(permuted_rows, expanded_idx_to_permuted_idx, expert_scales,
+                             shared_expert_output, H)
+    _rows_out(permuted_rows.dtype, T, H, residual, gamma, residual_out, norm_out)
+    _check(LIB.moe_finalize_rmsnorm_noalloc_run(
+        _ptr(permuted_rows), permuted_rows.shape[0], _ptr(expanded_idx_to_permuted_idx),
+        _ptr(expert_scales), sdt, _ptr(shared_expert_output), float(routed_scaling_factor),
+        _ptr(residual), _ptr(gamma), float(eps), _ptr(residual_out), _ptr(norm_out),
         T, H, K, act, _stream(residual, stream)))
 
 

@@ -571,6 +571,14 @@ __global__ __launch_bounds__(256) void stream_floor_kernel(const uint8_t* src, u
     __builtin_amdgcn_raw_buffer_store_b128(fold, wr, j * 16u, 0, 2);
 }
 
+// Zeroes n16 16-byte chunks at p (grid-stride): clears the static scratch of the allocation-free
+// entry point on its first use on a device.
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint8_t* p, uint32_t n16) {
+  const uint32_t stride = gridDim.x * 256u;
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n16; i += stride)
+    *(u32x4*)(p + (size_t)i * 16) = u32x4{0u, 0u, 0u, 0u};
+}
+
 // ------------------------------------------------------------------------------------------------
 // Host side: launch configuration and dispatch.
 // ------------------------------------------------------------------------------------------------
@@ -868,6 +876,52 @@ static int inputs_overlap(const Common& c, Range out) {
 
 static size_t workspace_bytes_for(int64_t T) { return kWsHeader + (size_t)T * kWsPerToken; }
 
+// Scratch of moe_finalize_rmsnorm_noalloc_run: the split-row exchange words of up to
+// kScratchTokens tokens in a file-scope device array, so that entry point allocates nothing and
+// takes no workspace. Each device holds its own copy until the process ends. In host code
+// `scratch` names a host-side stand-in, never the device memory: the device address is obtained
+// once per device with hipGetSymbolAddress (with that device current) and only that address is
+// passed to kernels.
+constexpr int64_t kScratchTokens = 1024;
+constexpr size_t kScratchBytes = kWsHeader + (size_t)kScratchTokens * kWsPerToken;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+static std::atomic<uint8_t*> g_scratch_ptr[kMaxDevices];
+static std::atomic<int> g_scratch_state[kMaxDevices];   // 0 new, 1 being set up, 2 ready
+
+// The current device's scratch address. On the first call on a device it is looked up, and a
+// kernel that zeroes the scratch is enqueued on `stream` ahead of the caller's work (the
+// exchange protocol starts from a zero-filled state; a kernel rather than a memset node, so a
+// graph captured around that first call replays correctly).
+static int scratch_for_current_device(hipStream_t stream, uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_FIN_ERR_HIP;
+  if (g_scratch_state[dev].load(std::memory_order_acquire) != 2) {
+    int expect = 0;
+    if (!g_scratch_state[dev].compare_exchange_strong(expect, 1, std::memory_order_acq_rel)) {
+      // another thread is setting this device up; wait for it (a few microseconds)
+      while (g_scratch_state[dev].load(std::memory_order_acquire) == 1) {
+      }
+      if (g_scratch_state[dev].load(std::memory_order_acquire) != 2) return MOE_FIN_ERR_HIP;
+    } else {
+      void* ptr = nullptr;
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+        g_scratch_state[dev].store(0, std::memory_order_release);
+        return MOE_FIN_ERR_HIP;
+      }
+      hipLaunchKernelGGL(zero_fill_kernel, dim3(64), dim3(256), 0, stream, (uint8_t*)ptr,
+                         (uint32_t)(kScratchBytes / 16));
+      if (hipGetLastError() != hipSuccess) {
+        g_scratch_state[dev].store(0, std::memory_order_release);
+        return MOE_FIN_ERR_HIP;
+      }
+      g_scratch_ptr[dev].store((uint8_t*)ptr, std::memory_order_release);
+      g_scratch_state[dev].store(2, std::memory_order_release);
+    }
+  }
+  *out = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  return MOE_FIN_OK;
+}
+
 static int run_rows(int mode, const Common& c, const void* residual, const void* gamma,
                     float eps, void* residual_out, void* norm_out, const float* qscale,
                     void* quant_out, void* scale_out, int sf_layout, void* workspace,
@@ -1069,6 +1123,9 @@ const char* moe_finalize_error_string(int code) {
     case MOE_FIN_ERR_WORKSPACE:
       return "workspace smaller than moe_finalize_workspace_size(num_tokens, hidden, top_k)";
     case MOE_FIN_ERR_POLICY: return "unknown cache policy";
+    case MOE_FIN_ERR_SCRATCH:
+      return "num_tokens above the 1024 that moe_finalize_rmsnorm_noalloc_run's static scratch "
+             "holds";
   }
   return "unknown error code";
 }
@@ -1207,6 +1264,30 @@ int moe_finalize_rmsnorm_run(const void* permuted_rows, int64_t num_permuted_row
   if (rc) return rc;
   return rmsnorm_call(c, residual, gamma, eps, residual_out, norm_out, workspace,
                       workspace_bytes, stream, 0);
+}
+
+int moe_finalize_rmsnorm_noalloc_run(const void* permuted_rows, int64_t num_permuted_rows,
+                                     const int32_t* expanded_idx_to_permuted_idx,
+                                     const void* expert_scales, int scales_dtype,
+                                     const void* shared_expert_output,
+                                     float routed_scaling_factor, const void* residual,
+                                     const void* gamma, float eps, void* residual_out,
+                                     void* norm_out, int64_t num_tokens, int64_t hidden,
+                                     int top_k, int act_dtype, void* stream) {
+  Common c{permuted_rows, num_permuted_rows, expanded_idx_to_permuted_idx, expert_scales,
+           scales_dtype, shared_expert_output, routed_scaling_factor, num_tokens, hidden,
+           top_k, act_dtype};
+  int rc = check_common(c, 8);
+  if (rc) return rc;
+  if (num_tokens > kScratchTokens) return MOE_FIN_ERR_SCRATCH;
+  if (hidden > 16384) return MOE_FIN_ERR_HIDDEN;
+  if (num_tokens == 0) return MOE_FIN_OK;
+  if ((rc = check_pointers(c))) return rc;
+  if ((rc = check_rows(c, residual, gamma, residual_out, norm_out, true))) return rc;
+  uint8_t* ws = nullptr;
+  if ((rc = scratch_for_current_device((hipStream_t)stream, &ws))) return rc;
+  return run_rows(MODE_RMS, c, residual, gamma, eps, residual_out, norm_out, nullptr, nullptr,
+                  nullptr, 0, ws, stream, 0);
 }
 
 int moe_residual_rmsnorm_run(const void* x, const void* residual, const void* gamma, float eps,

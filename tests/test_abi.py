@@ -393,3 +393,19 @@ def test_binding_rejects_mismatched_tensors():
         M.moe_rank_sum_rmsnorm_run(torch.zeros(T, H, dtype=bf), res, gam, 1e-6, None, out)
     with pytest.raises(ValueError, match=re.escape("residual must have shape")):
         M.moe_rank_sum_rmsnorm_run(torch.zeros(2, T, H, dtype=bf), res[:2], gam, 1e-6, None, out)
+
+
+def test_noalloc_entry_validation_codes():
+    """The allocation-free entry point checks its shape (including the static scratch's limit of
+    1024 tokens) before anything else; T = 0 is a no-op that needs no device."""
+    f = LIB.moe_finalize_rmsnorm_noalloc_run
+
+    def call(T=4, H=1024, K=8, rows=A, idx=B, no=D, act=0):
+        return f(rows, T * K, idx, None, 2, None, 1.0, E, E + 0x200000, 1e-6, None, no, T, H, K, act,
+                 None)
+
+    assert call(T=1025) == -13 and call(T=1 << 20) == -13
+    assert call(K=0) == -3 and call(H=1020) == -4 and call(H=16392) == -4 and call(act=5) == -6
+    assert call(T=-1) == -2
+    assert call(T=0) == 0
+    assert M.moe_finalize_error_string(-13).startswith("num_tokens above")
