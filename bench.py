@@ -143,6 +143,12 @@ def _parse():
     p.add_argument("--scan", action="store_true",
                    help="warm timings over a grid of uncommon shapes (performance-cliff check)")
     p.add_argument("--groups", default="", help="comma-separated sweep groups to run (default all)")
+    p.add_argument("--stream-sweep", action="store_true",
+                   help="only sweep the stream kernel's launch shape (loads per round, workgroup "
+                        "lanes, workgroups, nontemporal) cold at the T=64 and T=128 byte counts")
+    p.add_argument("--stream-shapes", default="",
+                   help="with --stream-sweep: only these shapes, 'loads:lanes:workgroups:nt,...' "
+                        "(workgroups 0 = one round)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
@@ -161,6 +167,10 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if a.stream_sweep:
+        print(json.dumps({"stream_sweep": _stream_sweep(torch, M, dev, a.stream_shapes)}),
+              flush=True)
+        return
     T, H, K = 128, 7168, 8
     inp = make_inputs(T, H, K, seed=workload_seed("larger", T))
     n_valid = int((inp.idx >= 0).sum())
@@ -319,6 +329,41 @@ def _stream_ceiling(torch, M, stream, dev, read_bytes, write_bytes, min_rotate=R
         s_, rb, d_, wb, stream=stream)) for s_, d_ in zip(srcs, dsts)], replays)
     del srcs, dsts
     return us
+
+
+def _stream_sweep(torch, M, dev, shapes=""):
+    """Cold µs per launch of the stream probe over launch shapes, at the byte counts of the
+    larger-decode workloads (T = 64 and 128, hidden 7168, top_k 8: reads / writes of the fused
+    RMSNorm call). Each shape is timed like the finalize: a graph of one launch per copy,
+    rotating over >= 2 GiB of copies, median of replays."""
+    T_cases = [(64, 7_358_464, 1_835_008), (128, 14_702_592, 3_670_016)]
+    if shapes:
+        todo = [tuple(int(v) for v in x.split(":")) for x in shapes.split(",")]
+    else:
+        todo = [(l, w, g, nt) for l in (1, 2, 4, 8, 16) for w in (256, 512, 1024)
+                for g in (0, 256, 512, 1024) for nt in (1, 0)]
+    stream = torch.cuda.Stream(device=dev)
+    out = []
+    for T, rb, wb in T_cases:
+        n = max(2, min(MAX_SETS, -(-ROTATE_BYTES // (rb + wb))))
+        srcs = [torch.ones(rb, dtype=torch.uint8, device=dev) for _ in range(n)]
+        dsts = [torch.empty(wb, dtype=torch.uint8, device=dev) for _ in range(n)]
+        for (loads, lanes, grid, nt) in todo:
+            g = grid or -(-(rb // 16) // (lanes * loads))
+            print(f"stream T={T} loads={loads} lanes={lanes} workgroups={g} nt={nt}",
+                  file=sys.stderr, flush=True)
+            us = _graph_us(torch, stream, [
+                (lambda s_=s_, d_=d_, g=g, loads=loads, lanes=lanes, nt=nt:
+                 M.moe_finalize_stream_probe_run(s_, rb, d_, wb, loads, lanes, g, bool(nt),
+                                                 stream=stream))
+                for s_, d_ in zip(srcs, dsts)], 10)
+            out.append({"T": T, "read_bytes": rb, "write_bytes": wb, "loads": loads,
+                        "lanes": lanes, "workgroups": g, "one_round": grid == 0,
+                        "nontemporal": nt, "us": round(us, 3),
+                        "frac_peak": round((rb + wb) / (us * 1e-6) / 1e9 / PEAK_GBS, 4)})
+        del srcs, dsts
+        torch.cuda.empty_cache()
+    return out
 
 
 def _graph_us(torch, stream, fns, replays):

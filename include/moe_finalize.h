@@ -56,8 +56,8 @@
  *     slices of its row; it stays 0 in normal use. A workgroup that gives up counts the missing
  *     partial sums as NaN, so its part of that token's norm_out is NaN (FP8 codes 0x7F; NVFP4
  *     block scales 0x7F with zero codes) instead of a wrong finite value; residual_out is not
- *     affected. No reset is needed afterwards (a late workgroup still finds its row's partials,
- *     and the next call works normally); the flag stays set until the caller clears it.
+ *     affected. No reset is needed afterwards (a workgroup that starts late still finds its row's
+ *     partials, and the next call works normally); the flag stays set until the caller clears it.
  *     Progress: a token's slices are consecutive workgroups and rows are split only while the
  *     grid stays near one workgroup per compute unit of the current device (its count is
  *     queried once per device), so workgroups dispatched before a waiting one never wait on it
@@ -153,7 +153,7 @@ int moe_finalize_rmsnorm_run(const void* permuted_rows, int64_t num_permuted_row
  * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same computation, kernels and results, with no workspace argument. It calls
  * no allocating routine; the split-row exchange uses a static scratch array inside the library,
- * 262,400 bytes per device (256 + 256 per token for up to 1024 tokens), which each GPU the
+ * 131,328 bytes per device (256 + 128 per token for up to 1024 tokens), which each GPU the
  * library runs on holds until the process ends. The first call on a device also enqueues, ahead
  * of its own work on `stream`, one small kernel that zeroes that device's scratch.
  *   num_tokens  0..1024; more gives MOE_FIN_ERR_SCRATCH (nothing is enqueued).
@@ -210,7 +210,7 @@ int moe_finalize_quant_run(const void* permuted_rows, int64_t num_permuted_rows,
 
 /*
  * moe_finalize_workspace_size -- bytes of workspace the RMSNorm entry points may use for a call
- * with this shape (256 + 256 per token). Host-only. Returns 0 for num_tokens < 0.
+ * with this shape (256 + 128 per token). Host-only. Returns 0 for num_tokens < 0.
  */
 size_t moe_finalize_workspace_size(int64_t num_tokens, int64_t hidden, int top_k);
 
@@ -372,13 +372,29 @@ int64_t moe_finalize_set_wait_limit(int64_t polls);
  *   src  device memory, 16-byte aligned, read_bytes bytes (may be NULL if read_bytes == 0).
  *   dst  device memory, 16-byte aligned, write_bytes bytes, overlapping no part of src. Content
  *        written: with L = 256 * max(256, ceil(read_bytes / 16384)) lanes, 16-byte chunk j of dst
- *        is the XOR of chunks (j % L) + i*L, i = 0..3, of src (chunks past the end read as 0).
+ *        is the XOR of the chunks c of src with c % L == j % L (chunks past the end read as 0).
+ * It is moe_finalize_stream_probe_run with 4 loads per round, 256-lane workgroups,
+ * max(256, ceil(read_bytes / 16384)) workgroups and nontemporal accesses.
  * read_bytes and write_bytes must be multiples of 16 and at most 2^31. Errors:
  * MOE_FIN_ERR_BAD_SHAPE, MOE_FIN_ERR_NULL_POINTER, MOE_FIN_ERR_ALIGNMENT, MOE_FIN_ERR_ALIAS,
  * MOE_FIN_ERR_HIP. Both sizes 0 is a successful no-op.
  */
 int moe_finalize_stream_floor_run(const void* src, size_t read_bytes, void* dst,
                                   size_t write_bytes, void* stream);
+
+/*
+ * moe_finalize_stream_probe_run -- measurement aid: the stream kernel of
+ * moe_finalize_stream_floor_run with its launch shape chosen by the caller, to find the fastest
+ * single launch that moves a given number of bytes. `workgroups` workgroups of `workgroup_lanes`
+ * lanes (64, 128, 256, 512 or 1024; L = workgroups * workgroup_lanes lanes in all) read src in
+ * rounds of `loads_per_round` 128-bit loads per lane in flight (1, 2, 4, 8 or 16): lane l reads
+ * every chunk c with c % L == l. 16-byte chunk j of dst is the XOR of the chunks c of src with
+ * c % L == j % L. nontemporal != 0 marks every access nontemporal. Other arguments, limits and
+ * errors as moe_finalize_stream_floor_run (1 <= workgroups <= 65536, else MOE_FIN_ERR_BAD_SHAPE).
+ */
+int moe_finalize_stream_probe_run(const void* src, size_t read_bytes, void* dst,
+                                  size_t write_bytes, int loads_per_round, int workgroup_lanes,
+                                  int64_t workgroups, int nontemporal, void* stream);
 
 /* Static, NUL-terminated description of a return code. Host-only. */
 const char* moe_finalize_error_string(int code);

@@ -27,7 +27,7 @@ EXPORTED = ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_
             "moe_residual_rmsnorm_run", "moe_finalize_stream_floor_run",
             "moe_rank_sum_rmsnorm_run", "moe_rank_sum_quant_run", "moe_finalize_launch_config",
             "moe_finalize_set_cache_policy", "moe_finalize_set_wait_limit",
-            "moe_finalize_rmsnorm_noalloc_run")
+            "moe_finalize_rmsnorm_noalloc_run", "moe_finalize_stream_probe_run")
 
 _ACT = {torch.bfloat16: MOE_DTYPE_BF16, torch.float16: MOE_DTYPE_FP16}
 _SCALE = {torch.float32: MOE_DTYPE_FP32, torch.bfloat16: MOE_DTYPE_BF16}
@@ -79,6 +79,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_finalize_set_wait_limit.restype = i64
     lib.moe_finalize_stream_floor_run.argtypes = [vp, sz, vp, sz, vp]
     lib.moe_finalize_stream_floor_run.restype = ctypes.c_int
+    lib.moe_finalize_stream_probe_run.argtypes = [vp, sz, vp, sz, i32, i32, i64, i32, vp]
+    lib.moe_finalize_stream_probe_run.restype = ctypes.c_int
     lib.moe_rank_sum_rmsnorm_run.argtypes = [vp, i32, vp, vp, f32, vp, vp, vp, sz, i64, i64, i32,
                                              vp]
     lib.moe_rank_sum_rmsnorm_run.restype = ctypes.c_int
@@ -160,6 +162,18 @@ def moe_finalize_stream_floor_run(src: torch.Tensor, read_bytes: int, dst: torch
             raise ValueError("byte count exceeds the tensor")
     _check(LIB.moe_finalize_stream_floor_run(_ptr(src), int(read_bytes), _ptr(dst),
                                              int(write_bytes), _stream(dst, stream)))
+
+
+def moe_finalize_stream_probe_run(src: torch.Tensor, read_bytes: int, dst: torch.Tensor,
+                                  write_bytes: int, loads_per_round: int, workgroup_lanes: int,
+                                  workgroups: int, nontemporal: bool = True, stream=None) -> None:
+    for t, n in ((src, read_bytes), (dst, write_bytes)):
+        if n > t.numel() * t.element_size():
+            raise ValueError("byte count exceeds the tensor")
+    _check(LIB.moe_finalize_stream_probe_run(_ptr(src), int(read_bytes), _ptr(dst),
+                                             int(write_bytes), int(loads_per_round),
+                                             int(workgroup_lanes), int(workgroups),
+                                             1 if nontemporal else 0, _stream(dst, stream)))
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:

@@ -74,26 +74,20 @@ struct Params {
 // Split rows. When a token's row is spread over `slices` workgroups, each workgroup publishes
 // the sum of squares of its slice in the caller's workspace and waits for the other slices of
 // its token. Layout: a 256-byte header whose first word is a sticky timeout flag, then one
-// 256-byte block per token: kMaxSlices 64-bit slots (bytes 0..127, one cache line), then the
-// token's 32-bit epoch word and 32-bit arrival count (bytes 128 and 132, a line of their own).
-// A slot carries (epoch << 32 | float bits of a partial) in ONE relaxed device-scope atomic word,
-// so the flag and the data become visible together and no release/acquire fences (L2 writeback /
-// invalidate) are needed. Every slice of a call reads the token's epoch E at its start,
-// publishes E + 1 in its own slot, adds itself to the arrival count, and waits until slots
-// 0..slices-1 carry E + 1. The slice whose addition completes the count (all slices have read E
-// by then: each added itself after publishing E + 1, which depends on its read) resets the count
-// and stores E + 1 as the token's epoch; the next call on the stream starts after this one ends
-// and sees it. So the epoch advances exactly when every slice of the call has read it, even when
-// a slice runs late: a late slice still reads E, finds the others' E + 1 and completes. A slot
-// holds at most the token's current epoch between calls, so stale slots of a call with more
-// slices never match. A zero-filled workspace is valid, no call needs a reset (also after a
-// timeout), the slice count may change from call to call, and a call writes only the slots it
-// uses and one line of epoch and count per token. When a slice gives up waiting (spin_limit
-// polls), it sets the header flag and counts the missing partials as NaN, so its part of
-// norm_out (and of the quantized outputs) is NaN rather than a wrong finite value; residual_out
-// is unaffected.
+// 128-byte block (one cache line) per token holding kMaxSlices 64-bit slots. A slot carries
+// (epoch << 32 | float bits of a partial) in ONE relaxed device-scope atomic word, so the flag and
+// the data become visible together and no release/acquire fences (L2 writeback / invalidate) are
+// needed. All kMaxSlices slots of a token hold the same epoch between calls: slice j rewrites
+// every slot m with m % slices == j (its own slot j carries its partial), so a call reads the
+// current epoch from its own slot and waits until slots 0..slices-1 carry epoch + 1. Only slice j
+// writes the slots m == j (mod slices), so a slice that starts late still reads the old epoch,
+// finds the others' new one and completes, leaving every slot on the new epoch. A zero-filled
+// workspace is valid, no call needs a reset (also after a timeout), and the slice count may
+// change from call to call. When a slice gives up waiting (spin_limit polls), it sets the header
+// flag and counts the missing partials as NaN, so its part of norm_out (and of the quantized
+// outputs) is NaN rather than a wrong finite value; residual_out is unaffected.
 constexpr int kMaxSlices = 16;
-constexpr size_t kWsHeader = 256, kWsPerToken = 256, kWsEpochOffset = 128, kWsCountOffset = 132;
+constexpr size_t kWsHeader = 256, kWsPerToken = 8 * kMaxSlices;
 constexpr uint32_t kMaxSpins = 1u << 22;      // ~0.1-0.5 s of polling, then give up (flagged)
 constexpr uint32_t kQuietNaN = 0x7FC00000u;
 
@@ -271,14 +265,19 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
       (uint32_t)lane64 * 2u, 0, 0);
   [[maybe_unused]] double qs = 0.0;
   if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) qs = (double)*a.qscale;
-  // Split rows: the token's current epoch, read now so the barrier does not wait for it. Every
-  // wavefront reads it unconditionally (from gamma, a valid dummy, when rows are whole): a load
-  // under a branch would make the compiler wait for it at the branch join.
+  // Split rows: this slice's current epoch (the upper half of its exchange word), read now so the
+  // barrier does not wait for it. Every wavefront reads it unconditionally (from gamma, a valid
+  // dummy, when rows are whole): a load under a branch would make the compiler wait for it at the
+  // branch join. Only the 32 bits in use are loaded: with a 64-bit load the compiler reused the
+  // unused half's register at once, and that wait held the first row load back until this
+  // memory-side load had returned.
   [[maybe_unused]] uint32_t epoch_prev = 0;
   if constexpr (MODE != MODE_FIN) {
     const uint32_t* ep =
-        a.slices > 1 ? (const uint32_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken + kWsEpochOffset)
-                     : (const uint32_t*)a.gamma;
+        a.slices > 1
+            ? (const uint32_t*)((const uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken) +
+                                slice) + 1
+            : (const uint32_t*)a.gamma;
     epoch_prev = __hip_atomic_load(ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
@@ -431,16 +430,14 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     for (int i = 0; i < n_waves0; ++i)
       tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, part), i));
     if (a.slices > 1) {
-      uint8_t* const blk = a.ws + kWsHeader + (size_t)t * kWsPerToken;
-      uint64_t* const slot = (uint64_t*)blk;
+      uint64_t* const slot = (uint64_t*)(a.ws + kWsHeader + (size_t)t * kWsPerToken);
       const int S = a.slices;
       const uint32_t epoch = epoch_prev + 1u;
-      uint32_t arrived = 0;
-      if (tid == 0) {
-        const uint64_t v = ((uint64_t)epoch << 32) | (uint64_t)__builtin_bit_cast(uint32_t, tot);
-        __hip_atomic_store(slot + slice, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        arrived = __hip_atomic_fetch_add((uint32_t*)(blk + kWsCountOffset), 1u, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
+      const int m = slice + tid * S;              // this slice's slots
+      if (m < kMaxSlices) {
+        const uint64_t v = ((uint64_t)epoch << 32) |
+                           (m == slice ? (uint64_t)__builtin_bit_cast(uint32_t, tot) : 0ull);
+        __hip_atomic_store(slot + m, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       // lane j < S waits for slice j's word of this epoch; a partial that never arrives counts
       // as NaN
@@ -465,13 +462,6 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
       tot = 0.f;
       for (int j = 0; j < S; ++j)                 // slice order: deterministic
         tot += __builtin_bit_cast(float, __builtin_amdgcn_readlane((int)bits, j));
-      // the last slice to arrive: every slice has read the old epoch
-      if (tid == 0 && arrived == (uint32_t)(S - 1)) {
-        __hip_atomic_store((uint32_t*)(blk + kWsCountOffset), 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store((uint32_t*)(blk + kWsEpochOffset), epoch, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
     }
     if (tid == 0) row_total = tot;
   }
@@ -545,30 +535,33 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantParams a) {
 __global__ __launch_bounds__(1024) void launch_floor_kernel(int) {}
 
 // Measurement aid: move n_rd 16-byte chunks in and n_wr chunks out in one launch, the way a
-// perfect finalize would (every load of a lane issued before any is used, nontemporal loads and
-// stores), with nothing else to do. Its time is the single-launch streaming ceiling for a given
-// number of bytes, which the finalize timings are compared against. Each lane reads up to
-// kStreamLoads chunks (lane + i * lanes), folds them with XOR, and stores the fold at every
-// output chunk j with j % lanes == lane; chunks past the end read zeros.
-constexpr int kStreamLoads = 4;
-__global__ __launch_bounds__(256) void stream_floor_kernel(const uint8_t* src, uint32_t n_rd,
-                                                           uint8_t* dst, uint32_t n_wr) {
-  const uint32_t lanes = gridDim.x * 256u;
-  const uint32_t lane = blockIdx.x * 256u + threadIdx.x;
+// perfect finalize would (every load of a round issued before any is used), with nothing else to
+// do. Its time is the single-launch streaming ceiling for a given number of bytes, which the
+// finalize timings are compared against. With `lanes` = grid x workgroup lanes, lane l reads, in
+// rounds of LOADS loads in flight, every chunk c with c % lanes == l (round r: chunks
+// l + (r * LOADS + i) * lanes), folds them with XOR, and stores the fold at every output chunk j
+// with j % lanes == l; chunks past the end read zeros. NT = 2 makes every access nontemporal.
+template <int LOADS, int NT>
+__global__ __launch_bounds__(1024) void stream_probe_kernel(const uint8_t* src, uint32_t n_rd,
+                                                            uint8_t* dst, uint32_t n_wr) {
+  const uint32_t lanes = gridDim.x * blockDim.x;
+  const uint32_t lane = blockIdx.x * blockDim.x + threadIdx.x;
   const auto rd = rsrc(src, n_rd * 16u);
   const auto wr = rsrc(dst, n_wr * 16u);
-  u32x4 v[kStreamLoads];
+  u32x4 fold = {0u, 0u, 0u, 0u};
+  for (uint32_t base = lane; base < n_rd; base += lanes * (uint32_t)LOADS) {
+    u32x4 v[LOADS];
 #pragma unroll
-  for (int i = 0; i < kStreamLoads; ++i)
-    v[i] = __builtin_amdgcn_raw_buffer_load_b128(rd, (lane + (uint32_t)i * lanes) * 16u, 0, 2);
-  u32x4 fold = v[0];
+    for (int i = 0; i < LOADS; ++i)
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rd, (base + (uint32_t)i * lanes) * 16u, 0, NT);
 #pragma unroll
-  for (int i = 1; i < kStreamLoads; ++i) fold ^= v[i];
+    for (int i = 0; i < LOADS; ++i) fold ^= v[i];
+  }
   // every lane consumes its loads here, so none is moved into the store loop (which lanes past
   // the last output chunk skip)
   asm volatile("" ::"v"(fold));
   for (uint32_t j = lane; j < n_wr; j += lanes)
-    __builtin_amdgcn_raw_buffer_store_b128(fold, wr, j * 16u, 0, 2);
+    __builtin_amdgcn_raw_buffer_store_b128(fold, wr, j * 16u, 0, NT);
 }
 
 // Zeroes n16 16-byte chunks at p (grid-stride): clears the static scratch of the allocation-free
@@ -1202,24 +1195,61 @@ int moe_finalize_launch_config(int entry, int64_t num_tokens, int64_t hidden, in
   return MOE_FIN_OK;
 }
 
-int moe_finalize_stream_floor_run(const void* src, size_t read_bytes, void* dst,
-                                  size_t write_bytes, void* stream) {
+// Shape checks and launch of the stream probe (both measurement entry points).
+static int stream_probe(const void* src, size_t read_bytes, void* dst, size_t write_bytes,
+                        int loads, int lanes, int64_t grid, int nontemporal, void* stream) {
   const size_t kMax = (size_t)1 << 31;
   if (read_bytes % 16 != 0 || write_bytes % 16 != 0 || read_bytes > kMax || write_bytes > kMax)
     return MOE_FIN_ERR_BAD_SHAPE;
+  if (loads != 1 && loads != 2 && loads != 4 && loads != 8 && loads != 16) return MOE_FIN_ERR_BAD_SHAPE;
+  if (lanes != 64 && lanes != 128 && lanes != 256 && lanes != 512 && lanes != 1024)
+    return MOE_FIN_ERR_BAD_SHAPE;
+  if (grid < 1 || grid > 65536) return MOE_FIN_ERR_BAD_SHAPE;
+  // every chunk offset a lane forms, base + i * lanes < 2^27 + 2^27 chunks, stays below 2^32 bytes
+  if (grid * lanes * loads > ((int64_t)1 << 27)) return MOE_FIN_ERR_BAD_SHAPE;
   if ((read_bytes && !src) || (write_bytes && !dst)) return MOE_FIN_ERR_NULL_POINTER;
   if (!aligned(src, 16) || !aligned(dst, 16)) return MOE_FIN_ERR_ALIGNMENT;
   if (read_bytes && write_bytes && overlap(rng(src, read_bytes), rng(dst, write_bytes)))
     return MOE_FIN_ERR_ALIAS;
   const uint32_t n_rd = (uint32_t)(read_bytes / 16), n_wr = (uint32_t)(write_bytes / 16);
   if (n_rd == 0 && n_wr == 0) return MOE_FIN_OK;
-  // one 256-lane workgroup per kStreamLoads * 256 chunks read, at least one per CU
-  const uint32_t per_wg = 256u * kStreamLoads;
-  uint32_t grid = (n_rd + per_wg - 1) / per_wg;
-  if (grid < 256u) grid = 256u;
-  hipLaunchKernelGGL(stream_floor_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
-                     (const uint8_t*)src, n_rd, (uint8_t*)dst, n_wr);
+  const dim3 g((unsigned)grid), b((unsigned)lanes);
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t* sp = (const uint8_t*)src;
+  uint8_t* dp = (uint8_t*)dst;
+#define MFIN_PROBE(L)                                                                          \
+  case L:                                                                                      \
+    if (nontemporal)                                                                           \
+      hipLaunchKernelGGL((stream_probe_kernel<L, 2>), g, b, 0, s, sp, n_rd, dp, n_wr);         \
+    else                                                                                       \
+      hipLaunchKernelGGL((stream_probe_kernel<L, 0>), g, b, 0, s, sp, n_rd, dp, n_wr);         \
+    break;
+  switch (loads) {
+    MFIN_PROBE(1)
+    MFIN_PROBE(2)
+    MFIN_PROBE(4)
+    MFIN_PROBE(8)
+    MFIN_PROBE(16)
+  }
+#undef MFIN_PROBE
   return to_code(hipGetLastError());
+}
+
+int moe_finalize_stream_floor_run(const void* src, size_t read_bytes, void* dst,
+                                  size_t write_bytes, void* stream) {
+  // one round of 4 nontemporal loads per lane, 256-lane workgroups, at least one per CU
+  const int64_t per_wg = 256 * 4;
+  int64_t grid = ((int64_t)(read_bytes / 16) + per_wg - 1) / per_wg;
+  if (grid < 256) grid = 256;
+  if (grid > 65536) return MOE_FIN_ERR_BAD_SHAPE;
+  return stream_probe(src, read_bytes, dst, write_bytes, 4, 256, grid, 1, stream);
+}
+
+int moe_finalize_stream_probe_run(const void* src, size_t read_bytes, void* dst,
+                                  size_t write_bytes, int loads_per_round, int workgroup_lanes,
+                                  int64_t workgroups, int nontemporal, void* stream) {
+  return stream_probe(src, read_bytes, dst, write_bytes, loads_per_round, workgroup_lanes,
+                      workgroups, nontemporal, stream);
 }
 
 int moe_finalize_run(const void* permuted_rows, int64_t num_permuted_rows,

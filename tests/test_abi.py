@@ -115,7 +115,7 @@ def test_rmsnorm_validation_codes():
     assert rms(res_out=D) == -9                # residual_out overlaps norm_out
     assert rms(T=0) == 0
     need = M.moe_finalize_workspace_size(4, 1024, 8)
-    assert need == 256 + 4 * 256
+    assert need == 256 + 4 * 128
     assert rms(ws=WS + 64, ws_bytes=need) == -5           # workspace must be 256-byte aligned
     assert rms(ws=WS, ws_bytes=need - 1) == -11           # too small
     assert rms(ws=E, ws_bytes=need) == -9                 # overlaps residual

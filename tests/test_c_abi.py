@@ -20,7 +20,7 @@ int main(void) {
     /* host-only helpers: sizes, error strings, version */
     if (moe_finalize_sf_size(64, 6144, MOE_SF_SWIZZLED_128x4) != (size_t)128 * 384) return 1;
     if (moe_finalize_sf_size(5, 48, MOE_SF_LINEAR) != 15) return 2;
-    if (moe_finalize_workspace_size(128, 7168, 8) != 256 + 256 * 128) return 3;
+    if (moe_finalize_workspace_size(128, 7168, 8) != 256 + 128 * 128) return 3;
     if (strcmp(moe_finalize_error_string(MOE_FIN_OK), "success") != 0) return 4;
     if (moe_finalize_version() < 100) return 5;
     /* validation happens before anything touches a device: a bad top_k, a bad hidden, T = 0 */

@@ -796,6 +796,17 @@ def test_two_kernel_path_equals_fused_when_exact(act):
     _norm_within_1ulp(np64(no_2), np64(no_f), act)
 
 
+def _stream_fold(src, rb, wb, lanes):
+    """Documented content of the stream kernels: chunk j of dst is the XOR of the source chunks c
+    with c % lanes == j % lanes."""
+    chunks = src.numpy().view(np.uint32).reshape(-1, 4)[: rb // 16]
+    fold = np.zeros((lanes, 4), dtype=np.uint32)
+    for start in range(0, len(chunks), lanes):
+        part = chunks[start:start + lanes]
+        fold[: len(part)] ^= part
+    return fold[np.arange(wb // 16) % lanes]
+
+
 @pytest.mark.parametrize("rb,wb", [(16 * 1000, 16 * 300), (14_680_064, 3_670_016),
                                    (16 * 5 * 262144 + 48, 16 * 70000), (0, 4096), (4096, 0)])
 def test_stream_floor_writes_documented_fold(rb, wb):
@@ -809,16 +820,32 @@ def test_stream_floor_writes_documented_fold(rb, wb):
     M.moe_finalize_stream_floor_run(sd, rb, dd, wb)
     torch.cuda.synchronize()
     got = dd.cpu().numpy()
-    chunks = src.numpy().view(np.uint32).reshape(-1, 4)[: rb // 16]
-    lanes = 256 * max(256, -(-rb // 16384))
-    fold = np.zeros((lanes, 4), dtype=np.uint32)
-    for i in range(4):
-        part = chunks[i * lanes:(i + 1) * lanes]
-        fold[: len(part)] ^= part
     n_wr = wb // 16
-    want = fold[np.arange(n_wr) % lanes]
+    want = _stream_fold(src, rb, wb, 256 * max(256, -(-rb // 16384)))
     assert np.array_equal(got[: n_wr * 4].view(np.uint32).reshape(-1, 4), want)
     assert np.all(got[n_wr * 4:] == -7)
+
+
+@pytest.mark.parametrize("loads,lanes,grid,nt", [(1, 64, 3, 0), (16, 1024, 5, 1), (4, 256, 1000, 1),
+                                                 (8, 512, 7, 0), (2, 128, 256, 1)])
+def test_stream_probe_writes_documented_fold(loads, lanes, grid, nt):
+    """The stream probe at other launch shapes (several rounds per lane, partial rounds, more
+    lanes than chunks): documented content, nothing past write_bytes; bad shapes are refused."""
+    rb, wb = 16 * 70001, 16 * 5003
+    _say(f"stream probe loads {loads} lanes {lanes} grid {grid} nt {nt}")
+    g = torch.Generator().manual_seed(loads * 1000 + grid)
+    src = torch.randint(0, 2 ** 31, (rb // 4,), generator=g, dtype=torch.int32)
+    dst = torch.full(((wb + 4096) // 4,), -7, dtype=torch.int32)
+    sd, dd = src.cuda(), dst.cuda()
+    M.moe_finalize_stream_probe_run(sd, rb, dd, wb, loads, lanes, grid, bool(nt))
+    torch.cuda.synchronize()
+    got = dd.cpu().numpy()
+    want = _stream_fold(src, rb, wb, lanes * grid)
+    assert np.array_equal(got[: wb // 4].view(np.uint32).reshape(-1, 4), want)
+    assert np.all(got[wb // 4:] == -7)
+    for bad in ((3, lanes, grid), (loads, 96, grid), (loads, lanes, 0), (16, 1024, 65536)):
+        with pytest.raises(M.MoeFinalizeError):
+            M.moe_finalize_stream_probe_run(sd, rb, dd, wb, *bad)
 
 
 # ---- cancellation / high dynamic range (float32 accumulation, rounded once) -----------------------
@@ -998,9 +1025,9 @@ def test_split_row_timeout_is_flagged_poisoned_and_bounded():
     finally:
         assert M.moe_finalize_set_wait_limit(-1) == 0
     assert M.moe_finalize_set_wait_limit(-1) == 1 << 22
-    # the epoch word advanced once per call and every arrival count is back to 0
-    blk = ws[256:512].view(torch.int32).cpu()
-    assert int(blk[32]) == 3 and int(blk[33]) == 0
+    # every slot of the token advanced once per call
+    slot_epochs = (ws[256:256 + 128].view(torch.int64).cpu() >> 32).numpy()
+    assert (slot_epochs == 3).all(), slot_epochs
     for clear_flag in (False, True):
         if clear_flag:
             ws[:4].zero_()
@@ -1014,14 +1041,12 @@ def test_split_row_timeout_is_flagged_poisoned_and_bounded():
 
 def test_split_row_epochs_are_per_token():
     """The exchange words of a split row: after calls with different slice counts on one
-    workspace, each token's epoch word counts the split calls that touched the token, its arrival
-    count is back to 0, and its slots 0..S-1 carry that epoch (the slots past S of the last call
-    hold older epochs)."""
+    workspace, all 16 slots of each token carry one epoch, the number of split calls that touched
+    the token, and slot j < S of the last call holds slice j's partial."""
     ws = workspace(64)
     ws.zero_()
     seq = [(1, 2048, 8), (4, 7168, 8), (1, 6144, 8), (64, 7168, 8), (1, 2048, 8)]
     count = {}
-    last_s = {}
     for T, H, K in seq:
         inp = make_inputs(T, H, K, seed=810 + T + H)
         S = M.moe_finalize_launch_config(1, T, H, K)["slices"]
@@ -1031,15 +1056,16 @@ def test_split_row_epochs_are_per_token():
         check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, "bf16")
         for t in range(T):
             count[t] = count.get(t, 0) + 1
-            last_s[t] = S
-    blocks = ws[256:256 + 64 * 256].view(64, 256).cpu()
+    blocks = ws[256:256 + 64 * 128].view(64, 16, 8).cpu()
+    words = blocks.view(torch.int64).view(64, 16).numpy()
     for t, n in count.items():
-        epoch = int(blocks[t, 128:132].view(torch.int32).item())
-        assert epoch == n, (t, epoch, n)
-        assert int(blocks[t, 132:136].view(torch.int32).item()) == 0
-        slot_epochs = (blocks[t, :128].view(torch.int64) >> 32).numpy()
-        assert (slot_epochs[:last_s[t]] == n).all(), (t, slot_epochs)
-        assert (slot_epochs[last_s[t]:] < n).all(), (t, slot_epochs)
+        assert ((words[t] >> 32) == n).all(), (t, words[t] >> 32, n)
+    # the last call (T=1, hidden 2048: two slices): the slices' partials sum to the row's sum of
+    # squares of residual_out, and slots 2..15 carry no partial
+    parts = (words[0] & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    R = np64(ro)
+    assert abs(float(parts[0]) + float(parts[1]) - float((R * R).sum())) <= 1e-4 * float((R * R).sum())
+    assert not parts[2:].any()
 
 
 # ---- one GPU's share of the cross-rank reduction (moe_rank_sum_*_run) -----------------------------
