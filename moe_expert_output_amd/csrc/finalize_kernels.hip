@@ -69,6 +69,7 @@ struct Params {
   int pad_blocks;            // NVFP4, swizzled scales: workgroups after the token ones that
                              // only zero the scale bytes of the padding rows
   uint32_t spin_limit;       // split rows: polls of a slice's word before the wait gives up
+  int split_quant;           // quantized outputs: route group 1 encodes half of the codes
 };
 
 // Split rows. When a token's row is spread over `slices` workgroups, each workgroup publishes
@@ -119,10 +120,15 @@ struct QuantDst {
 // NTQ: the aux bits of the FP8 code stores (the fused kernel passes its nontemporal choice:
 // same-box A/B, cold, FP8 at T = 64 / 128 / 512: 0.18 / 0.35 / 0.58 us faster; the NVFP4 code
 // stores, 4 bytes per lane, stay cacheable: nontemporal was 0.37 us slower at T = 512).
-template <int MODE, int NTQ = 0>
+// HALF (NVFP4 only): 0 encodes all 8 elements; 1 only elements 0..3 (and the block scales),
+// 2 only elements 4..7, for two wavefronts that share one lane's values (each needs all 8 for
+// the block amax).
+template <int MODE, int NTQ = 0, int HALF = 0>
 __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
                                                const __amdgpu_buffer_rsrc_t& q_r, uint32_t voff,
                                                bool live, int s, int t, const QuantDst& d) {
+  static_assert(HALF == 0 || MODE == MODE_NVFP4, "only the NVFP4 codes are split");
+  constexpr int E0 = HALF == 2 ? 4 : 0, E1 = HALF == 1 ? 4 : 8;
   if constexpr (MODE == MODE_FP8) {
     u32x2 q = {0u, 0u};
 #pragma unroll
@@ -152,11 +158,17 @@ __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
     const uint32_t sign_keep = nan_blk ? 0u : 1u;
     uint32_t word = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = E0; e < E1; ++e) {
       const uint32_t m = e2m1_code(__builtin_fabsf(nr[e]), gs, sf) & keep;
-      word |= (m | ((sign_bit(nr[e]) & sign_keep) << 3)) << (4 * e);
+      word |= (m | ((sign_bit(nr[e]) & sign_keep) << 3)) << (4 * (e - E0));
     }
-    __builtin_amdgcn_raw_buffer_store_b32(word, q_r, voff >> 2, 0, 0);
+    if constexpr (HALF == 0) {
+      __builtin_amdgcn_raw_buffer_store_b32(word, q_r, voff >> 2, 0, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b16((unsigned short)word, q_r,
+                                            (voff >> 2) + (HALF == 2 ? 2u : 0u), 0, 0);
+      if constexpr (HALF == 2) return;         // the block scales come from the other half
+    }
     // Scale bytes: lanes 8m..8m+7 hold blocks 4m'..4m'+3 (two lanes per block).
     const uint32_t sf_here = live ? sfc : 0u;
     const uint32_t b1 = __shfl_down(sf_here, 2, 64);
@@ -466,26 +478,64 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     if (tid == 0) row_total = tot;
   }
   lds_barrier();
+  // NVFP4 with two or more route groups in at most four wavefronts (a.split_quant): group 1,
+  // idle after the row sum, encodes elements 4..7 of every lane's slots from group 0's rounded
+  // norm values (handed over in LDS) while group 0 encodes elements 0..3.
+  constexpr bool kSplitQ = MODE == MODE_NVFP4 && G > 1;
+  [[maybe_unused]] const bool split_q = kSplitQ && a.split_quant;
+  [[maybe_unused]] const uint32_t qrow = MODE == MODE_FP8 ? (uint32_t)a.H : (uint32_t)a.H / 2u;
+  [[maybe_unused]] const auto q_r =
+      rsrc(a.quant_out + (int64_t)t * qrow, (MODE == MODE_FP8 || MODE == MODE_NVFP4) ? qrow : 0u);
+  [[maybe_unused]] u32x4* const n_lds = (u32x4*)lds_dyn;
+  if constexpr (kSplitQ) {
+    if (split_q && g == 1) {
+      lds_barrier();                            // group 0's rounded norm values are in LDS
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        float nr[8];
+        Act<ACT>::unpack(n_lds[p * L + lane], nr);
+        quantize_store<MODE, NT, kSplitQ ? 2 : 0>(nr, qs, q_r, voff[p], live[p],
+                                                  slot0 + lane + p * L, t,
+                                                  QuantDst{a.sf_out, a.H, a.sf_swizzled});
+      }
+      return;
+    }
+  }
   if (g != 0) return;
   const float rinv = __builtin_amdgcn_rsqf(__builtin_fmaf(row_total, a.inv_h, a.eps));
 
   const auto no_r = rsrc(a.out + tok_off, a.out ? row_bytes : 0u);
-  [[maybe_unused]] const uint32_t qrow = MODE == MODE_FP8 ? (uint32_t)a.H : (uint32_t)a.H / 2u;
-  [[maybe_unused]] const auto q_r =
-      rsrc(a.quant_out + (int64_t)t * qrow, (MODE == MODE_FP8 || MODE == MODE_NVFP4) ? qrow : 0u);
+  u32x4 n_pk[P];
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     float gm[8], n[8];
     Act<ACT>::unpack(gamv[p], gm);
 #pragma unroll
     for (int e = 0; e < 8; ++e) n[e] = (r[p][e] * rinv) * gm[e];
-    const u32x4 n_pk = Act<ACT>::pack(n);
-    __builtin_amdgcn_raw_buffer_store_b128(n_pk, no_r, voff[p], 0, NT);
-    if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) {
-      float nr[8];
-      Act<ACT>::unpack(n_pk, nr);               // quantize the rounded norm_out values
-      quantize_store<MODE, NT>(nr, qs, q_r, voff[p], live[p], slot0 + lane + p * L, t,
-                           QuantDst{a.sf_out, a.H, a.sf_swizzled});
+    n_pk[p] = Act<ACT>::pack(n);
+    __builtin_amdgcn_raw_buffer_store_b128(n_pk[p], no_r, voff[p], 0, NT);
+    if constexpr (kSplitQ) {
+      if (split_q) n_lds[p * L + lane] = n_pk[p];
+    }
+  }
+  if constexpr (MODE == MODE_NVFP4 || MODE == MODE_FP8) {
+    const QuantDst qd{a.sf_out, a.H, a.sf_swizzled};
+    if (split_q) {
+      lds_barrier();
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        float nr[8];
+        Act<ACT>::unpack(n_pk[p], nr);          // quantize the rounded norm_out values
+        quantize_store<MODE, NT, kSplitQ ? 1 : 0>(nr, qs, q_r, voff[p], live[p],
+                                                  slot0 + lane + p * L, t, qd);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        float nr[8];
+        Act<ACT>::unpack(n_pk[p], nr);
+        quantize_store<MODE, NT, 0>(nr, qs, q_r, voff[p], live[p], slot0 + lane + p * L, t, qd);
+      }
     }
   }
 }
@@ -953,6 +1003,12 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
   p.route_stride = route_stride;
   p.pad_blocks = pad_blocks;
   p.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  // Half of the NVFP4 codes go to route group 1 when the workgroup has at most four wavefronts,
+  // so each wavefront of the epilogue has a SIMD of its own. Same-box A/B, bit-identical
+  // outputs, hidden 6144 top_k 8: NVFP4 T = 1 / 16 4.75 -> 4.62 / 4.97 -> 4.81 us (two groups of
+  // two wavefronts); at T = 64 (two groups of three) it cost 0.08-0.10 us, and FP8, whose codes
+  // cost less, lost 0.05 us at T = 1.
+  p.split_quant = mode == MODE_NVFP4 && cfg.G >= 2 && cfg.G * cfg.L <= 256;
   hipStream_t s = (hipStream_t)stream;
   switch (mode) {
     case MODE_RMS: return to_code(dispatch<MODE_RMS>(c.act, p, cfg, s));
@@ -1235,14 +1291,14 @@ static int stream_probe(const void* src, size_t read_bytes, void* dst, size_t wr
   return to_code(hipGetLastError());
 }
 
+// The fastest shape of a cold launch-shape sweep on MI355X at 9.2 and 18.4 MB (loads per round
+// 1..16, 256..1024-lane workgroups, 256..3590 workgroups, nontemporal or not): one load per round,
+// four 512-lane workgroups per CU, nontemporal. 18.4 MB: 4.28 us against 4.45 for the next shape
+// and 4.61 for one round of four loads in 256-lane workgroups; 9.2 MB: 2.88 us, within 0.02 us
+// of the best.
 int moe_finalize_stream_floor_run(const void* src, size_t read_bytes, void* dst,
                                   size_t write_bytes, void* stream) {
-  // one round of 4 nontemporal loads per lane, 256-lane workgroups, at least one per CU
-  const int64_t per_wg = 256 * 4;
-  int64_t grid = ((int64_t)(read_bytes / 16) + per_wg - 1) / per_wg;
-  if (grid < 256) grid = 256;
-  if (grid > 65536) return MOE_FIN_ERR_BAD_SHAPE;
-  return stream_probe(src, read_bytes, dst, write_bytes, 4, 256, grid, 1, stream);
+  return stream_probe(src, read_bytes, dst, write_bytes, 1, 512, 1024, 1, stream);
 }
 
 int moe_finalize_stream_probe_run(const void* src, size_t read_bytes, void* dst,

@@ -821,7 +821,7 @@ def test_stream_floor_writes_documented_fold(rb, wb):
     torch.cuda.synchronize()
     got = dd.cpu().numpy()
     n_wr = wb // 16
-    want = _stream_fold(src, rb, wb, 256 * max(256, -(-rb // 16384)))
+    want = _stream_fold(src, rb, wb, 1024 * 512)
     assert np.array_equal(got[: n_wr * 4].view(np.uint32).reshape(-1, 4), want)
     assert np.all(got[n_wr * 4:] == -7)
 
