@@ -145,10 +145,12 @@ __device__ __forceinline__ uint32_t sign_bit(float x) {
 // (codes 0..7), saturate at 6; 0 for NaN. No division: each decision compares a*gs with
 // m*sf for a rounding midpoint m. m*sf is exact in float32 (a 3-bit by 4-bit product), and
 // fma(a, gs, -m*sf) rounds the exact difference a*gs - m*sf once, so its sign is the exact
-// sign: a nonzero difference is at least 2^-42 in magnitude (a*gs carries at most 32
-// significant bits and m*sf >= 2^-11), far above the float32 subnormals. Each test is the sign
-// bit of one FMA: no compare result goes through VCC, and the seven tests of a lane's eight
-// elements overlap.
+// sign unless that difference underflows to zero. It cannot: near a decision a*gs is close to
+// m*sf >= 2^-11, and a*gs carries at most 35 significant bits (an fp16 significand of 11 bits
+// times a float32 one of 24; bf16 gives 32), so both are multiples of about 2^-46 there and a
+// nonzero difference is at least that large, far above the float32 subnormals; far from a
+// decision the difference is large anyway. Each test is the sign bit of one FMA: no compare
+// result goes through VCC, and the seven tests of a lane's eight elements overlap.
 __device__ __forceinline__ uint32_t e2m1_code(float a, float gs, float sf) {
   // ties to the even code: midpoints 0.25, 1.25, 2.5, 5 go down (count a*gs > m*sf);
   // 0.75, 1.75, 3.5 go up (count a*gs >= m*sf, i.e. 1 - [a*gs < m*sf])
