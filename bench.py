@@ -119,6 +119,10 @@ def timing_plan(steps: int, warmup: int, n_sets: int) -> dict:
     replay also uploads it to the device, a one-time cost of ~10 us that would otherwise land in
     the timed region), then a graph that makes one call on each of the n_sets copies in order is
     replayed ceil(warmup / n_sets) times (at least once), so at least `warmup` calls run untimed.
+    The last warm-up replay is enqueued after the host synchronizes, right before the first
+    event, so the GPU is running when the timed graph is queued behind it: the timed calls see
+    the steady state of back-to-back calls (clocks up, launch latency overlapped) rather than a
+    start from idle, which at 20 calls added ~0.3-0.7 us per call.
     Copy i was last read n_sets - i calls before the timed graph reads it (the warm-up ends on
     copy n_sets - 1), and n_sets copies are 8x the Infinity Cache, so every timed call reads its
     inputs from HBM."""
@@ -149,6 +153,10 @@ def _parse():
     p.add_argument("--stream-shapes", default="",
                    help="with --stream-sweep: only these shapes, 'loads:lanes:workgroups:nt,...' "
                         "(workgroups 0 = one round)")
+    p.add_argument("--stream-tokens", default="64,128",
+                   help="with --stream-sweep: which byte counts (T = 64 and / or 128)")
+    p.add_argument("--stream-repeats", type=int, default=1,
+                   help="with --stream-sweep: time every shape this many times")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     return p.parse_args()
@@ -168,8 +176,9 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     if a.stream_sweep:
-        print(json.dumps({"stream_sweep": _stream_sweep(torch, M, dev, a.stream_shapes)}),
-              flush=True)
+        print(json.dumps({"stream_sweep": _stream_sweep(
+            torch, M, dev, a.stream_shapes, [int(t) for t in a.stream_tokens.split(",")],
+            a.stream_repeats)}), flush=True)
         return
     T, H, K = 128, 7168, 8
     inp = make_inputs(T, H, K, seed=workload_seed("larger", T))
@@ -215,12 +224,14 @@ def main():
             call(sets[i])
     with torch.cuda.stream(stream):
         timed_graph.replay()                       # untimed: uploads the timed graph
-        for _ in range(plan["warmup_replays"]):
+        for _ in range(plan["warmup_replays"] - 1):
             warm_graph.replay()
         torch.cuda.synchronize()
         t_host0 = time.perf_counter()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
+        # the last warm-up replay keeps the GPU busy while the timed graph is enqueued behind it
+        warm_graph.replay()
         ev0.record(stream)
         timed_graph.replay()
         ev1.record(stream)
@@ -331,12 +342,13 @@ def _stream_ceiling(torch, M, stream, dev, read_bytes, write_bytes, min_rotate=R
     return us
 
 
-def _stream_sweep(torch, M, dev, shapes=""):
+def _stream_sweep(torch, M, dev, shapes="", tokens=(64, 128), repeats=1):
     """Cold µs per launch of the stream probe over launch shapes, at the byte counts of the
     larger-decode workloads (T = 64 and 128, hidden 7168, top_k 8: reads / writes of the fused
     RMSNorm call). Each shape is timed like the finalize: a graph of one launch per copy,
     rotating over >= 2 GiB of copies, median of replays."""
-    T_cases = [(64, 7_358_464, 1_835_008), (128, 14_702_592, 3_670_016)]
+    T_cases = [c for c in [(64, 7_358_464, 1_835_008), (128, 14_702_592, 3_670_016)]
+               if c[0] in tokens]
     if shapes:
         todo = [tuple(int(v) for v in x.split(":")) for x in shapes.split(",")]
     else:
@@ -348,7 +360,7 @@ def _stream_sweep(torch, M, dev, shapes=""):
         n = max(2, min(MAX_SETS, -(-ROTATE_BYTES // (rb + wb))))
         srcs = [torch.ones(rb, dtype=torch.uint8, device=dev) for _ in range(n)]
         dsts = [torch.empty(wb, dtype=torch.uint8, device=dev) for _ in range(n)]
-        for (loads, lanes, grid, nt) in todo:
+        for (loads, lanes, grid, nt) in [x for _ in range(repeats) for x in todo]:
             g = grid or -(-(rb // 16) // (lanes * loads))
             print(f"stream T={T} loads={loads} lanes={lanes} workgroups={g} nt={nt}",
                   file=sys.stderr, flush=True)
