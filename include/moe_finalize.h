@@ -312,7 +312,10 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
  * (num_cus <= 0: the current device's count, which only this case queries; with a workspace the
  * slice rule depends on it). Host-only; launches nothing. Writes MOE_FIN_LAUNCH_CONFIG_FIELDS
  * int64 values to `out` (n_out is the caller's array length):
- *   out[0] workgroups in the grid (0 when num_tokens == 0); a swizzled NVFP4 call whose
+ *   out[0] workgroups in the grid (0 when num_tokens == 0): num_tokens * out[2], or for split
+ *          rows with cacheable accesses (out[7] == 0) ceil(num_tokens / 8) * 8 * out[2] (the
+ *          slices of a token share one of the 8 XCDs, and the workgroups of the padding tokens
+ *          exit at once); a swizzled NVFP4 call whose
  *          num_tokens is not a multiple of 128 adds a few workgroups after these that only
  *          zero the scale bytes of the padding rows
  *   out[1] lanes per workgroup (route groups x lanes per group, a multiple of 64, <= 1024)

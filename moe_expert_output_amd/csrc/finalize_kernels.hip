@@ -70,6 +70,8 @@ struct Params {
                              // only zero the scale bytes of the padding rows
   uint32_t spin_limit;       // split rows: polls of a slice's word before the wait gives up
   int split_quant;           // quantized outputs: route group 1 encodes half of the codes
+  int main_blocks;           // workgroups before the scale-padding ones
+  int xcd_map;               // split rows: a token's slices share one XCD (see token_slice)
 };
 
 // Split rows. When a token's row is spread over `slices` workgroups, each workgroup publishes
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   // their wavefronts are idle). They wait on nothing, so no split row's exchange waits on them.
   const int bid = blockIdx.x;
   if constexpr (MODE == MODE_NVFP4) {
-    const int n_main = a.T * a.slices;
+    const int n_main = a.main_blocks;
     if (bid >= n_main) {
       zero_sf_padding(QuantDst{a.sf_out, a.H, 1}, a.T,
                       (int64_t)(bid - n_main) * blockDim.x + threadIdx.x,
@@ -234,8 +236,22 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
       return;
     }
   }
-  const int t = bid / a.slices;
-  const int slice = bid - t * a.slices;
+  // Workgroup -> (token, slice). Workgroup b runs on XCD b % 8, so with a.xcd_map the slices of
+  // token t are the workgroups (g * slices + j) * 8 + t % 8 (g = t / 8): all on one XCD, where
+  // they start together, instead of on consecutive XCDs, whose start times differ by up to
+  // ~0.5 us that the exchange would wait for (the host's xcd_mapped chooses when). Workgroups
+  // of tokens past T (T not a multiple of 8) exit at once.
+  int t, slice;
+  if (a.xcd_map) {
+    const int q = bid >> 3;
+    const int grp = q / a.slices;
+    slice = q - grp * a.slices;
+    t = (grp << 3) + (bid & 7);
+    if (t >= a.T) return;
+  } else {
+    t = bid / a.slices;
+    slice = bid - t * a.slices;
+  }
   const int tid = threadIdx.x;
   const int L = a.lanes;
   const int g = __builtin_amdgcn_readfirstlane(tid / L);   // wave-uniform route group
@@ -666,6 +682,28 @@ static int device_cus(int* cus) {
 // Polls of a split row's exchange word before a slice gives up (moe_finalize_set_wait_limit).
 static std::atomic<uint32_t> g_spin_limit{kMaxSpins};
 
+// Split rows of calls with cacheable accesses put the slices of a token on one XCD (workgroups
+// are dealt to the 8 XCDs of gfx950 round-robin): the grid then has ceil(T / 8) * 8 * slices
+// workgroups, those of tokens past T idle. Slices on consecutive XCDs start up to ~0.5 us
+// apart (per-workgroup s_memrealtime timeline, T = 1 hidden 6144: 0.53 us median spread of the
+// six slices' starts, 1.0 us median exchange), and the exchange waits for the last one.
+// Same-box A/B, bit-identical outputs, top_k 8, median of replays:
+//   inputs in the caches (the pages' protocol): T = 1 / 4 / 8 / 16 / 24 / 32 4.10 -> 3.74 /
+//     4.19 -> 3.79 / 4.24 -> 3.95 / 4.12 -> 4.02 / 4.26 -> 4.06 / 4.28 -> 4.10 us; NVFP4 T = 1
+//     4.79 -> 4.48; FP8 T = 16 4.60 -> 4.36;
+//   inputs from HBM: T = 4 4.19 -> 3.94, but T = 8 / 16 / 24 / 32 / 64 +0.12 / +0.18 / +0.17 /
+//     +0.21 / +0.36 us, T = 128 within 0.05.
+// So the placement follows the cache policy's own assumption: calls with cacheable accesses
+// (below 4 MiB of rows under AUTO; the decode batches a pipeline reads right after the expert
+// GEMM wrote them) co-locate the slices; nontemporal calls (inputs assumed in HBM) do not.
+constexpr int kXcds = 8;
+static bool xcd_mapped(int mode, const Config& c) {
+  return mode != 0 && c.grid_x > 1 && !c.nontemporal;
+}
+static int64_t main_blocks(int mode, const Config& c, int64_t T) {
+  return xcd_mapped(mode, c) ? (T + kXcds - 1) / kXcds * kXcds * c.grid_x : (int64_t)c.grid_x * T;
+}
+
 static int next_pow2(int x) {
   int p = 1;
   while (p < x) p <<= 1;
@@ -778,7 +816,7 @@ static bool make_config(int mode, int64_t T, int H, int K, int slices, Config* c
 
 template <int ACT, int MODE, int G, int P, int JMAX>
 static hipError_t launch_one(const Params& p, const Config& c, hipStream_t s) {
-  dim3 grid((unsigned)(c.grid_x * p.T + p.pad_blocks));
+  dim3 grid((unsigned)(p.main_blocks + p.pad_blocks));
   dim3 block(c.G * c.L);
   if (c.nontemporal)
     hipLaunchKernelGGL((finalize_kernel<ACT, MODE, G, P, JMAX, 2>), grid, block, c.lds, s, p);
@@ -985,7 +1023,8 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
       mode == MODE_NVFP4 && sf_layout == MOE_SF_SWIZZLED_128x4 && c.T % 128 != 0
           ? (int)((((c.H / 16 + 3) / 4) * 128 + 2 * cfg.G * cfg.L - 1) / (2 * cfg.G * cfg.L))
           : 0;
-  if ((int64_t)cfg.grid_x * c.T + pad_blocks > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
+  const int64_t n_main = main_blocks(mode, cfg, c.T);
+  if (n_main + pad_blocks > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
   Params p = base_params(c);
   p.residual = (const uint8_t*)residual;
   p.gamma = (const uint8_t*)gamma;
@@ -999,6 +1038,8 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
   p.lanes = cfg.L;
   p.slot_span = cfg.span;
   p.slices = cfg.grid_x;
+  p.main_blocks = (int)n_main;
+  p.xcd_map = xcd_mapped(mode, cfg) ? 1 : 0;
   p.ws = (uint8_t*)workspace;
   p.route_stride = route_stride;
   p.pad_blocks = pad_blocks;
@@ -1216,7 +1257,7 @@ static int entry_config(int entry, int64_t num_tokens, int64_t hidden, int top_k
   if (!make_config(entry == 0 ? MODE_FIN : MODE_RMS, T, (int)hidden, top_k, slices, c))
     return MOE_FIN_ERR_HIDDEN;
   c->nontemporal = use_nontemporal(T, hidden, top_k);
-  if ((int64_t)c->grid_x * T > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
+  if (main_blocks(entry == 0 ? MODE_FIN : MODE_RMS, *c, T) > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
   return MOE_FIN_OK;
 }
 
@@ -1226,7 +1267,9 @@ int moe_finalize_launch_floor_run(int entry, int64_t num_tokens, int64_t hidden,
   // (T = 0 only validates the shape: no slice rule, so no device query)
   const int rc = entry_config(entry, num_tokens, hidden, top_k, num_tokens > 0, 0, &c);
   if (rc || num_tokens == 0) return rc;
-  hipLaunchKernelGGL(launch_floor_kernel, dim3((unsigned)(c.grid_x * num_tokens)), dim3(c.G * c.L),
+  hipLaunchKernelGGL(launch_floor_kernel,
+                     dim3((unsigned)main_blocks(entry == 0 ? MODE_FIN : MODE_RMS, c, num_tokens)),
+                     dim3(c.G * c.L),
                      c.lds, (hipStream_t)stream, 0);
   return to_code(hipGetLastError());
 }
@@ -1239,7 +1282,7 @@ int moe_finalize_launch_config(int entry, int64_t num_tokens, int64_t hidden, in
   const int rc =
       entry_config(entry, num_tokens, hidden, top_k, with_workspace != 0, num_cus, &c);
   if (rc) return rc;
-  out[0] = (int64_t)c.grid_x * num_tokens;
+  out[0] = num_tokens > 0 ? main_blocks(entry == 0 ? MODE_FIN : MODE_RMS, c, num_tokens) : 0;
   out[1] = (int64_t)c.G * c.L;
   out[2] = entry > 0 ? c.grid_x : 1;
   out[3] = c.G;
@@ -1328,6 +1371,7 @@ int moe_finalize_run(const void* permuted_rows, int64_t num_permuted_rows,
   cfg.nontemporal = use_nontemporal(num_tokens, hidden, top_k);
   if ((int64_t)cfg.grid_x * num_tokens > INT32_MAX) return MOE_FIN_ERR_BAD_SHAPE;
   Params p = base_params(c);
+  p.main_blocks = (int)(cfg.grid_x * num_tokens);
   p.out = (uint8_t*)out;
   p.lanes = cfg.L;
   p.slot_span = cfg.span;
