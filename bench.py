@@ -298,6 +298,12 @@ def main():
                      "stream_ceiling_GBs": round(nbytes / (ceil_us * 1e-6) / 1e9, 1),
                      "frac_of_stream_ceiling": round(ceil_us / us_per_call, 4)},
     }
+    # The other configurations of the metric in brief: decode T = 1 / 4 / 16 (hidden 6144) warm,
+    # against the launch floor; T = 64 (hidden 7168) cold; the same generators and protocols as
+    # --sweep, which covers every configuration in full.
+    del sets
+    torch.cuda.empty_cache()
+    out["other_configs"] = _brief(torch, M, stream, dev)
     if a.sweep:
         out["cases"] = _sweep(torch, M, stream, dev, large=not a.no_large,
                               groups=[g for g in a.groups.split(",") if g],
@@ -308,6 +314,51 @@ def main():
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = _cpu_baseline(inp, nbytes, a.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def _brief(torch, M, stream, dev):
+    """Decode T = 1 / 4 / 16 at hidden 6144 (warm µs/call, launch floor, excess) and T = 64 at
+    hidden 7168 (cold µs/call, GB/s, fraction of 8 TB/s and of the stream ceiling)."""
+    from synth import make_inputs, workload_seed
+    ws = torch.zeros(M.moe_finalize_workspace_size(64, 0, 0), dtype=torch.uint8, device=dev)
+    res = []
+    for T, H, grp in ((1, 6144, "decode"), (4, 6144, "decode"), (16, 6144, "decode"),
+                      (64, 7168, "larger")):
+        inp = make_inputs(T, H, 8, seed=workload_seed(grp, T))
+        n_valid = int((inp.idx >= 0).sum())
+        nb = algorithmic_bytes(T, H, 8, n_valid)
+        cold = T >= 32
+        n = max(2, min(MAX_SETS, -(-ROTATE_BYTES // _set_bytes(inp)))) if cold else 1
+        sets = [_dev_set(torch, inp, dev) for _ in range(n)]
+
+        def fn(d):
+            return lambda: M.moe_finalize_rmsnorm_run(
+                d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf, d["residual"],
+                d["gamma"], inp.eps, d["ro"], d["no"], ws, stream=stream)
+        r = {"workload": f"moe_finalize_rmsnorm T={T} hidden {H} top_k 8 bf16", "T": T, "H": H,
+             "bytes": nb}
+        if cold:
+            us = _graph_us(torch, stream, [fn(d) for d in sets], 20)
+            rd = _read_bytes(T, H, 8, n_valid)
+            del sets
+            ceil_us = _stream_ceiling(torch, M, stream, dev, rd, nb - rd)
+            r.update({"protocol": "cold", "us_per_call": round(us, 3),
+                      "gbs": round(nb / (us * 1e-6) / 1e9, 1),
+                      "frac_peak": round(nb / (us * 1e-6) / 1e9 / PEAK_GBS, 4),
+                      "stream_ceiling_us": round(ceil_us, 3),
+                      "frac_of_stream_ceiling": round(ceil_us / us, 4)})
+        else:
+            us = _warm_us(torch, stream, fn(sets[0]))
+            floor = _warm_us(torch, stream, lambda T=T, H=H: M.moe_finalize_launch_floor_run(
+                1, T, H, 8, device=dev, stream=stream))
+            del sets
+            r.update({"protocol": "warm (20 calls on one input set, median of 50 replays)",
+                      "us_per_call": round(us, 3), "launch_floor_us": round(floor, 3),
+                      "excess_over_floor_us": round(us - floor, 3)})
+        res.append(r)
+        torch.cuda.empty_cache()
+    assert int(ws[:4].view(torch.int32).item()) == 0, "a split row timed out"
+    return res
 
 
 def _headline_kernel(M, T, H, K):
@@ -497,8 +548,10 @@ def _sweep(torch, M, stream, dev, large=True, groups=(), cpu=False):
     ws_big = torch.zeros(M.moe_finalize_workspace_size(max(c[2] for c in todo), 0, 0),
                          dtype=torch.uint8, device=dev)
     for (grp, entry, T, H, K, act, sdt, sh, quant) in todo:
-        print(f"sweep {grp} {entry} T={T} H={H} K={K} {act} {sdt} {quant or ''}", file=sys.stderr,
-              flush=True)
+        # the clock readings let a profiler's dispatch timestamps be assigned to the case
+        print(f"sweep {grp} {entry} T={T} H={H} K={K} {act} {sdt} {quant or ''} "
+              f"mono_ns={time.monotonic_ns()} boot_ns={time.clock_gettime_ns(time.CLOCK_BOOTTIME)}",
+              file=sys.stderr, flush=True)
         kvar = K if grp == "highk" else None
         inp = make_inputs(T, H, K, act_dtype=act, scale_dtype=sdt, with_shared=sh,
                           seed=workload_seed(grp, T, act, sdt, kvar),
