@@ -335,7 +335,8 @@ def sf_size(T: int, H: int, layout: int) -> int:
 def sf_offset(t: int, b: int, H: int, layout: int) -> int:
     """Byte offset of the scale of (row t, block b). SWIZZLED_128x4 tiles rows by 128 and blocks by
     4; a 512-byte tile holds row r = t % 128 at (r % 32) * 16 + (r // 32) * 4 and block b % 4 in
-    the last position; tiles run along the blocks of a row tile first."""
+    the last position; tiles run along the blocks of a row tile first. This is the cuBLAS
+    block-scaling-factor layout; the tests check it byte for byte against PyTorch's to_blocked."""
     nb = H // NVFP4_BLOCK
     if layout == SF_LINEAR:
         return t * nb + b

@@ -111,8 +111,8 @@ def test_sf_layout_size_bijection_padding():
 def test_sf_layout_tile_structure():
     # Within one 128-row x 4-block tile of 512 bytes, 4 consecutive blocks of a row are 4
     # consecutive bytes, and rows r, r+32, r+64, r+96 share one 16-byte line. Tiles of the same
-    # row band follow each other along the blocks. (Parity of this byte map against an outside
-    # producer is unpinned: the pages name the layout but never print it.)
+    # row band follow each other along the blocks. (The pages name the layout but never print
+    # it; test_sf_swizzled_map_matches_torch_to_blocked checks the map against PyTorch's.)
     H = 16 * 12
     for t in range(128):
         base = O.sf_offset(t, 0, H, 1)
@@ -164,3 +164,47 @@ def test_nonfinite_inputs_follow_the_stated_reading():
     assert sf[3] == 0x7E and c4[63] == 0xF              # -inf: code -6
     q8 = O.quant_fp8(np.array([[inf, -inf, nan, -nan, 1.0, -0.0, 500.0, -500.0]]), 1.0)[0]
     assert list(q8) == [0x7E, 0xFE, 0x7F, 0x7F, 0x38, 0x80, 0x7E, 0xFE]
+
+
+def _torch_to_blocked():
+    """PyTorch's own producer of the 128x4 block-scaling-factor layout (`to_blocked` in
+    torch/testing/_internal/common_quantized.py, with its `ceil_div`), an implementation
+    independent of the oracle's. That module imports test utilities that are not installed
+    here, so only these two functions are compiled from its source file."""
+    import ast
+    import os
+
+    import torch
+    path = os.path.join(os.path.dirname(torch.__file__), "testing", "_internal",
+                        "common_quantized.py")
+    if not os.path.exists(path):
+        pytest.skip("torch's common_quantized.py is not in this torch build")
+    tree = ast.parse(open(path).read())
+    funcs = [n for n in tree.body if isinstance(n, ast.FunctionDef)
+             and n.name in ("ceil_div", "to_blocked")]
+    if len(funcs) != 2:
+        pytest.skip("this torch build has no to_blocked")
+    ns = {"torch": torch}
+    exec(compile(ast.Module(body=funcs, type_ignores=[]), path, "exec"), ns)
+    return ns["to_blocked"]
+
+
+@pytest.mark.parametrize("TH", [(1, 64), (5, 48), (130, 96), (64, 6144), (128, 7168), (300, 2064),
+                                (257, 16)])
+def test_sf_swizzled_map_matches_torch_to_blocked(TH):
+    """The oracle's SWIZZLED_128x4 byte map against an outside producer of the layout: scale
+    (t, b) of a [T, H/16] scale matrix lands at the byte torch's to_blocked puts it, and every
+    other byte of the padded buffer is padding (zero)."""
+    import torch
+    to_blocked = _torch_to_blocked()
+    T, H = TH
+    nb = H // 16
+    ids = torch.arange(1, T * nb + 1, dtype=torch.int64).view(T, nb)   # a unique id per scale
+    flat = to_blocked(ids).numpy()
+    assert flat.size == O.sf_size(T, H, O.SF_SWIZZLED_128x4)
+    offs = np.array([[O.sf_offset(t, b, H, O.SF_SWIZZLED_128x4) for b in range(nb)]
+                     for t in range(T)])
+    assert np.array_equal(flat[offs], ids.numpy())
+    pad = np.ones(flat.size, bool)
+    pad[offs.ravel()] = False
+    assert not flat[pad].any()
