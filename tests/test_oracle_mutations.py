@@ -16,7 +16,7 @@ from tests import test_oracle_quant_pins as Q
 
 _orig = {name: getattr(R, name) for name in
          ("finalize_unrounded", "round_to_format", "residual_rmsnorm", "quant_nvfp4",
-          "sf_offset")}
+          "sf_offset", "reference_unrounded", "finalize_magnitude")}
 
 
 def _fin_no_rsf(rows, idx, scales, shared, rsf):
@@ -91,6 +91,38 @@ def _sf_offset_transposed(t, b, H, layout):
         tile * 512 + (r % 32) * 16 + (r // 32) * 4 + (b % 4)
 
 
+def _sf_offset_rows_in_order(t, b, H, layout):
+    # rows of a 128-row tile in plain order (4 bytes each) instead of the 32 x 4 interleave
+    if layout == R.SF_LINEAR:
+        return _orig["sf_offset"](t, b, H, layout)
+    nb = H // 16
+    n_col_tiles = (nb + 3) // 4
+    tile = (t // 128) * n_col_tiles + b // 4
+    return tile * 512 + (t % 128) * 4 + (b % 4)
+
+
+def _ref_eps_outside(rows, idx, scales, shared, rsf, residual, gamma, eps):
+    res, _ = _orig["reference_unrounded"](rows, idx, scales, shared, rsf, residual, gamma, eps)
+    ms = np.mean(res * res, axis=-1, keepdims=True)
+    return res, res / (np.sqrt(ms) + float(np.float32(eps))) * np.asarray(gamma, np.float64)
+
+
+def _ref_sum_not_mean(rows, idx, scales, shared, rsf, residual, gamma, eps):
+    res, _ = _orig["reference_unrounded"](rows, idx, scales, shared, rsf, residual, gamma, eps)
+    ms = np.sum(res * res, axis=-1, keepdims=True)
+    return res, res / np.sqrt(ms + float(np.float32(eps))) * np.asarray(gamma, np.float64)
+
+
+def _ref_no_residual(rows, idx, scales, shared, rsf, residual, gamma, eps):
+    return _orig["reference_unrounded"](rows, idx, scales, shared, rsf, np.zeros_like(residual),
+                                        gamma, eps)
+
+
+def _mag_signed_shared(rows, idx, scales, shared, rsf):
+    out = _orig["finalize_magnitude"](rows, idx, scales, None, rsf)
+    return out if shared is None else out + np.asarray(shared, dtype=np.float64)
+
+
 MUTANTS = [
     ("finalize_unrounded", _fin_no_rsf, [P.test_finalize_exact_bruteforce,
                                          P.test_dyadic_fixture_closed_form]),
@@ -105,6 +137,11 @@ MUTANTS = [
     ("residual_rmsnorm", _rms_unrounded_input, [P.test_rmsnorm_correctly_rounded_bruteforce]),
     ("quant_nvfp4", _nvfp4_nibbles_swapped, [Q.test_nvfp4_exact_bruteforce]),
     ("sf_offset", _sf_offset_transposed, [Q.test_sf_layout_tile_structure]),
+    ("sf_offset", _sf_offset_rows_in_order, [Q.test_sf_swizzled_map_matches_torch_to_blocked]),
+    ("reference_unrounded", _ref_eps_outside, [P.test_reference_unrounded_and_magnitude_bruteforce]),
+    ("reference_unrounded", _ref_sum_not_mean, [P.test_reference_unrounded_and_magnitude_bruteforce]),
+    ("reference_unrounded", _ref_no_residual, [P.test_reference_unrounded_and_magnitude_bruteforce]),
+    ("finalize_magnitude", _mag_signed_shared, [P.test_reference_unrounded_and_magnitude_bruteforce]),
 ]
 
 _ARGS = {
@@ -112,6 +149,8 @@ _ARGS = {
     P.test_round_matches_exact_bruteforce: [("bf16",), ("fp16",)],
     P.test_rmsnorm_correctly_rounded_bruteforce: [("bf16",)],
     Q.test_nvfp4_exact_bruteforce: [(R.SF_SWIZZLED_128x4,)],
+    Q.test_sf_swizzled_map_matches_torch_to_blocked: [((130, 96),), ((300, 2064),)],
+    P.test_reference_unrounded_and_magnitude_bruteforce: [("bf16", 61), ("fp16", 62)],
 }
 
 

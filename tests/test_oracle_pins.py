@@ -314,3 +314,52 @@ def test_pages_tp4_accuracy_figures():
     assert 4.7e-3 <= floor <= 4.95e-3, floor
     assert 5.85e-3 <= new <= 6.15e-3, new
     assert 7.6e-3 <= old <= 8.0e-3, old
+
+
+# ------------------------------------------------------------------------------------------------
+# The unrounded reference (the accuracy reports' baseline) and the magnitude behind the float32
+# window: pinned by exact rational brute force on tiny inputs.
+@pytest.mark.parametrize("act,seed", [("bf16", 61), ("fp16", 62), ("bf16", 63)])
+def test_reference_unrounded_and_magnitude_bruteforce(act, seed):
+    """residual = RSF * sum of w * x over present routes + shared + residual, norm = residual *
+    gamma / sqrt(mean(residual^2) + eps) with no rounding anywhere, and the magnitude |RSF| * sum
+    |w * x| + |shared|, against Fractions (the square root taken last, in float64 of the exact
+    radicand)."""
+    T, H, K = 3, 16, 5
+    inp = make_inputs(T, H, K, seed=seed, act_dtype=act, n_rows=T * K + 2)
+    inp.idx[1, 2] = -1
+    inp.idx[2, :] = -1                       # a token with no present route
+    f = lambda t: t.double().numpy()  # noqa: E731
+    rows, idx, sc, sh = f(inp.rows), inp.idx.numpy(), f(inp.scales), f(inp.shared)
+    res, gam = f(inp.residual), f(inp.gamma)
+    eps = float(np.float32(inp.eps))
+    rsf = Fraction(inp.rsf)
+    ref_res, ref_norm = O.reference_unrounded(rows, idx, sc, sh, inp.rsf, res, gam, inp.eps)
+    mag = O.finalize_magnitude(rows, idx, sc, sh, inp.rsf)
+    for t in range(T):
+        acc = [Fraction(0)] * H
+        mg = [Fraction(0)] * H
+        for k in range(K):
+            p = int(idx[t, k])
+            if 0 <= p < rows.shape[0]:
+                w = Fraction(float(sc[t, k]))
+                for h in range(H):
+                    term = w * Fraction(float(rows[p, h]))
+                    acc[h] += term
+                    mg[h] += abs(term)
+        R = [rsf * acc[h] + Fraction(float(sh[t, h])) + Fraction(float(res[t, h])) for h in range(H)]
+        M = [abs(rsf) * mg[h] + abs(Fraction(float(sh[t, h]))) for h in range(H)]
+        ms = sum(r * r for r in R) / H
+        root = math.sqrt(float(ms + Fraction(eps)))
+        for h in range(H):
+            assert ref_res[t, h] == pytest.approx(float(R[h]), rel=1e-13, abs=1e-300)
+            want = float(R[h] * Fraction(float(gam[h]))) / root
+            assert ref_norm[t, h] == pytest.approx(want, rel=1e-12, abs=1e-300)
+            assert mag[t, h] == pytest.approx(float(M[h]), rel=1e-13, abs=1e-300)
+    # the window's magnitude bounds the sum, with equality when every term is non-negative
+    S = O.finalize_unrounded(rows, idx, sc, sh, inp.rsf)
+    assert np.all(mag >= np.abs(S) * (1 - 1e-15))
+    pos = make_inputs(2, 16, 4, seed=seed + 100, act_dtype=act)
+    pr, ps, psh = np.abs(f(pos.rows)), np.abs(f(pos.scales)), np.abs(f(pos.shared))
+    assert np.allclose(O.finalize_magnitude(pr, pos.idx.numpy(), ps, psh, 2.5),
+                       O.finalize_unrounded(pr, pos.idx.numpy(), ps, psh, 2.5), rtol=1e-15, atol=0)
