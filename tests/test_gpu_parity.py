@@ -922,7 +922,8 @@ def _guards_intact(full):
     return bool((g[:GUARD] == 0x5A).all() and (g[-GUARD:] == 0x5A).all())
 
 
-@pytest.mark.parametrize("THK", [(5, 1032, 8), (37, 7168, 8), (130, 2048, 22), (3, 48, 6)])
+@pytest.mark.parametrize("THK", [(5, 1032, 8), (37, 7168, 8), (130, 2048, 22), (3, 48, 6), (5, 4096, 8),
+                                 (1, 6144, 8)])
 def test_outputs_stay_in_bounds_and_inputs_untouched(THK):
     T, H, K = THK
     _say(f"guards T={T} H={H} K={K}")
