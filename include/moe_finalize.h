@@ -174,6 +174,19 @@ int moe_finalize_rmsnorm_noalloc_run(const void* permuted_rows, int64_t num_perm
                                      int top_k, int act_dtype, void* stream);
 
 /*
+ * moe_finalize_workspace_flag -- host query of a workspace's timeout flag (see "Workspace"):
+ * *flag = its first 32-bit word, nonzero if a split-row wait of an earlier call gave up. With
+ * workspace == NULL, the flag of the current device's static scratch of
+ * moe_finalize_rmsnorm_noalloc_run (0 if that entry point has not run on the device). clear != 0
+ * also resets a set flag to zero (a 16-byte fill kernel on `stream`; the split-row slots need
+ * no reset). Enqueues a 4-byte copy on `stream` and waits for that stream, so the calls before
+ * it on the stream are counted; a diagnostic for the host, not for a captured graph. Errors:
+ * MOE_FIN_ERR_NULL_POINTER (flag), MOE_FIN_ERR_ALIGNMENT (workspace not 256-byte aligned),
+ * MOE_FIN_ERR_HIP.
+ */
+int moe_finalize_workspace_flag(const void* workspace, int clear, int* flag, void* stream);
+
+/*
  * moe_finalize_quant_run -- moe_finalize_rmsnorm_run followed by quantization of norm
  * ([FI3385] walkthrough: FP8 / NVFP4 quantized outputs with an output scale and a layout code;
  * [FI6631] test changes: the NVFP4 scale buffer is sized for SWIZZLED_128x4).

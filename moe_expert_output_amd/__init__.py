@@ -13,6 +13,6 @@ from .binding import (  # noqa: F401
     moe_finalize_run,
     moe_finalize_set_cache_policy, moe_finalize_set_wait_limit, moe_finalize_sf_size,
     moe_finalize_stream_floor_run, moe_finalize_stream_probe_run, moe_finalize_version,
-    moe_finalize_workspace_size,
+    moe_finalize_workspace_flag, moe_finalize_workspace_size,
     moe_quantize_run, moe_rank_sum_quant_run, moe_rank_sum_rmsnorm_run, moe_residual_rmsnorm_run,
 )

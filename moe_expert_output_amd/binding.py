@@ -27,7 +27,8 @@ EXPORTED = ("moe_finalize_run", "moe_finalize_rmsnorm_run", "moe_finalize_quant_
             "moe_residual_rmsnorm_run", "moe_finalize_stream_floor_run",
             "moe_rank_sum_rmsnorm_run", "moe_rank_sum_quant_run", "moe_finalize_launch_config",
             "moe_finalize_set_cache_policy", "moe_finalize_set_wait_limit",
-            "moe_finalize_rmsnorm_noalloc_run", "moe_finalize_stream_probe_run")
+            "moe_finalize_rmsnorm_noalloc_run", "moe_finalize_stream_probe_run",
+            "moe_finalize_workspace_flag")
 
 _ACT = {torch.bfloat16: MOE_DTYPE_BF16, torch.float16: MOE_DTYPE_FP16}
 _SCALE = {torch.float32: MOE_DTYPE_FP32, torch.bfloat16: MOE_DTYPE_BF16}
@@ -81,6 +82,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_finalize_stream_floor_run.restype = ctypes.c_int
     lib.moe_finalize_stream_probe_run.argtypes = [vp, sz, vp, sz, i32, i32, i64, i32, vp]
     lib.moe_finalize_stream_probe_run.restype = ctypes.c_int
+    lib.moe_finalize_workspace_flag.argtypes = [vp, i32, ctypes.POINTER(i32), vp]
+    lib.moe_finalize_workspace_flag.restype = ctypes.c_int
     lib.moe_rank_sum_rmsnorm_run.argtypes = [vp, i32, vp, vp, f32, vp, vp, vp, sz, i64, i64, i32,
                                              vp]
     lib.moe_rank_sum_rmsnorm_run.restype = ctypes.c_int
@@ -153,6 +156,24 @@ def moe_finalize_set_wait_limit(polls: int) -> int:
     """Set the process-wide poll limit of split-row waits (< 0: the default); returns the
     previous limit."""
     return int(LIB.moe_finalize_set_wait_limit(int(polls)))
+
+
+def moe_finalize_workspace_flag(workspace: Optional[torch.Tensor] = None, clear: bool = False,
+                                stream=None) -> int:
+    """The timeout flag of a workspace, or with workspace None of the current device's static
+    scratch of moe_finalize_rmsnorm_noalloc_run (waits for the stream); clear resets it."""
+    flag = ctypes.c_int(0)
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < 256:
+            raise ValueError("workspace must hold at least its 256-byte header")
+        s = _stream(workspace, stream)
+    elif stream is not None:
+        s = int(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+    else:
+        s = torch.cuda.current_stream().cuda_stream
+    _check(LIB.moe_finalize_workspace_flag(_ptr(workspace), 1 if clear else 0, ctypes.byref(flag),
+                                           s))
+    return int(flag.value)
 
 
 def moe_finalize_stream_floor_run(src: torch.Tensor, read_bytes: int, dst: torch.Tensor,

@@ -1420,6 +1420,36 @@ int moe_finalize_rmsnorm_noalloc_run(const void* permuted_rows, int64_t num_perm
                   nullptr, 0, ws, stream, 0);
 }
 
+int moe_finalize_workspace_flag(const void* workspace, int clear, int* flag, void* stream) {
+  if (!flag) return MOE_FIN_ERR_NULL_POINTER;
+  const void* src = workspace;
+  if (!src) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_FIN_ERR_HIP;
+    // the static scratch of moe_finalize_rmsnorm_noalloc_run; never used yet on this device: 0
+    if (g_scratch_state[dev].load(std::memory_order_acquire) != 2) {
+      *flag = 0;
+      return MOE_FIN_OK;
+    }
+    src = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  } else if (!aligned(workspace, 256)) {
+    return MOE_FIN_ERR_ALIGNMENT;
+  }
+  uint32_t v = 0;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(&v, src, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MOE_FIN_ERR_HIP;
+  *flag = (int)v;
+  if (clear && v) {
+    // the flag's 16-byte unit of the header; the rest of the header is unused
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(1), dim3(256), 0, s, (uint8_t*)src, 1u);
+    if (hipGetLastError() != hipSuccess || hipStreamSynchronize(s) != hipSuccess)
+      return MOE_FIN_ERR_HIP;
+  }
+  return MOE_FIN_OK;
+}
+
 int moe_residual_rmsnorm_run(const void* x, const void* residual, const void* gamma, float eps,
                              void* residual_out, void* norm_out, void* workspace,
                              size_t workspace_bytes, int64_t num_tokens, int64_t hidden,

@@ -412,3 +412,16 @@ def test_noalloc_entry_validation_codes():
     assert call(T=-1) == -2
     assert call(T=0) == 0
     assert M.moe_finalize_error_string(-13).startswith("num_tokens above")
+
+
+def test_workspace_flag_validation_codes():
+    """The flag query rejects a null result pointer and a misaligned workspace before touching the
+    device."""
+    import torch
+
+    f = LIB.moe_finalize_workspace_flag
+    v = ctypes.c_int(5)
+    assert f(A, 0, None, None) == -1
+    assert f(A + 4, 0, ctypes.byref(v), None) == -5 and v.value == 5
+    with pytest.raises(ValueError):
+        M.moe_finalize_workspace_flag(torch.zeros(0, dtype=torch.uint8))

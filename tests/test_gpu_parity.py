@@ -1004,6 +1004,7 @@ def test_split_row_timeout_is_flagged_poisoned_and_bounded():
                                    d["residual"], d["gamma"], inp.eps, ro, no, ws)
         torch.cuda.synchronize()
         assert int(ws[:4].view(torch.int32).item()) == 1
+        assert M.moe_finalize_workspace_flag(ws) == 1
         check_residual(np64(ro), ref, np64(inp.residual), "bf16")
         assert torch.isnan(no.float()).all()
         ro2 = torch.empty_like(ro)
@@ -1031,7 +1032,8 @@ def test_split_row_timeout_is_flagged_poisoned_and_bounded():
     assert (slot_epochs == 3).all(), slot_epochs
     for clear_flag in (False, True):
         if clear_flag:
-            ws[:4].zero_()
+            assert M.moe_finalize_workspace_flag(ws, clear=True) == 1
+            assert M.moe_finalize_workspace_flag(ws) == 0
         M.moe_finalize_rmsnorm_run(d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf,
                                    d["residual"], d["gamma"], inp.eps, ro, no, ws)
         torch.cuda.synchronize()

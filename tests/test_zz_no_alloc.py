@@ -1,7 +1,8 @@
 """The allocation-free entry point (moe_finalize_rmsnorm_noalloc_run): through the C ABI, two
 calls in a row (the second on a smaller input) give the same bits as moe_finalize_rmsnorm_run with
 a zero-filled workspace, and meet the oracle's bars; num_tokens above its static scratch's limit is
-rejected before anything is enqueued."""
+rejected before anything is enqueued; a forced split-row timeout sets the static scratch's flag,
+which the host reads and clears through moe_finalize_workspace_flag."""
 from __future__ import annotations
 
 import numpy as np
@@ -68,3 +69,36 @@ def test_noalloc_whole_rows_and_limit():
     assert e.value.code == -13
     torch.cuda.synchronize()
     assert (ro.float() == 7.0).all() and (no.float() == 7.0).all()
+
+
+def test_noalloc_scratch_flag_reads_and_clears():
+    """Failure detection on the static scratch, forced from the host with a wait limit of 0 polls:
+    norm_out comes out NaN, residual_out stays exact, the flag reads 1 and clears; the next call
+    with the default limit is correct again without any reset of the scratch."""
+    inp = make_inputs(1, 2048, 8, seed=911)                                  # 2 slices per row
+    assert M.moe_finalize_launch_config(1, 1, 2048, 8)["slices"] == 2
+    d = to_dev(inp)
+    ref = oracle_ref(inp)
+    ro = torch.empty(1, 2048, dtype=torch.bfloat16, device="cuda")
+    no = torch.empty_like(ro)
+    args = (d["rows"], d["idx"], d["scales"], d["shared"], inp.rsf, d["residual"], d["gamma"],
+            inp.eps, ro, no)
+    M.moe_finalize_rmsnorm_noalloc_run(*args)
+    assert M.moe_finalize_workspace_flag() == 0
+    print("noalloc: forcing split-row timeouts with a wait limit of 0 polls", flush=True)
+    prev = M.moe_finalize_set_wait_limit(0)
+    try:
+        M.moe_finalize_rmsnorm_noalloc_run(*args)
+        torch.cuda.synchronize()
+    finally:
+        assert M.moe_finalize_set_wait_limit(-1) == 0
+    assert prev == 1 << 22
+    check_residual(np64(ro), ref, np64(inp.residual), "bf16")
+    assert torch.isnan(no.float()).all()
+    assert M.moe_finalize_workspace_flag(clear=True) == 1
+    assert M.moe_finalize_workspace_flag() == 0
+    M.moe_finalize_rmsnorm_noalloc_run(*args)
+    torch.cuda.synchronize()
+    assert M.moe_finalize_workspace_flag() == 0
+    check_residual(np64(ro), ref, np64(inp.residual), "bf16")
+    check_norm(np64(no), np64(ro), ref, np64(inp.gamma), inp.eps, "bf16")
