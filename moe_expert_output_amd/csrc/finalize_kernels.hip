@@ -42,36 +42,40 @@ namespace mfin {
 enum : int { MODE_FIN = 0, MODE_RMS = 1, MODE_NVFP4 = 2, MODE_FP8 = 3 };
 
 struct Params {
-  const uint8_t* rows;       // [n_rows, H] act dtype
-  int64_t n_rows;
+  // The launch shape and what the first loads address, together at the front so that they
+  // arrive in one batch of scalar loads (see the start of finalize_kernel).
+  int T, H, K;
+  int slices;                // workgroups per token (> 1: the row is split, see below)
+  int xcd_map;               // split rows: a token's slices share one XCD (see token_slice)
+  int main_blocks;           // workgroups before the scale-padding ones
+  int route_stride;          // > 0: no route map; route k of token t is row k * route_stride + t
+  int scales_bf16;
+  int nv;                    // H / 8 slots per row
+  int lanes;                 // L: lanes per route group (multiple of 64)
+  int slot_span;             // slots covered by one workgroup (L * P)
+  int pad_blocks;            // NVFP4, swizzled scales: workgroups after the token ones that
+                             // only zero the scale bytes of the padding rows
+  uint32_t slice_magic;      // ceil(2^32 / slices) where q * slices < 2^32 for every workgroup
+                             // index q, so q / slices = mulhi(q, slice_magic); else 0
   const int32_t* idx;        // [T, K]
   const void* scales;        // [T, K] fp32 or bf16, or null
-  int scales_bf16;
   const uint8_t* shared;     // [T, H] or null
-  float rsf;
   const uint8_t* residual;   // [T, H]
   const uint8_t* gamma;      // [H]
+  uint8_t* ws;               // workspace of the split row modes (null when slices == 1)
+  const uint8_t* rows;       // [n_rows, H] act dtype
+  int64_t n_rows;
+  float rsf;
   float eps;
   float inv_h;
+  int sf_swizzled;
   uint8_t* out;              // MODE_FIN: finalize output; else norm_out (nullable in quant)
   uint8_t* residual_out;     // nullable
   uint8_t* quant_out;
   uint8_t* sf_out;
   const float* qscale;
-  int sf_swizzled;
-  int T, H, K;
-  int nv;                    // H / 8 slots per row
-  int lanes;                 // L: lanes per route group (multiple of 64)
-  int slot_span;             // slots covered by one workgroup (L * P)
-  int slices;                // workgroups per token (> 1: the row is split, see below)
-  uint8_t* ws;               // workspace of the split row modes (null when slices == 1)
-  int route_stride;          // > 0: no route map; route k of token t is row k * route_stride + t
-  int pad_blocks;            // NVFP4, swizzled scales: workgroups after the token ones that
-                             // only zero the scale bytes of the padding rows
   uint32_t spin_limit;       // split rows: polls of a slice's word before the wait gives up
   int split_quant;           // quantized outputs: route group 1 encodes half of the codes
-  int main_blocks;           // workgroups before the scale-padding ones
-  int xcd_map;               // split rows: a token's slices share one XCD (see token_slice)
 };
 
 // Split rows. When a token's row is spread over `slices` workgroups, each workgroup publishes
@@ -226,6 +230,16 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   // padding rows (same-box A/B: after the token workgroups beat before them by up to 0.2 us at
   // T = 64, and beat zeroing in the token workgroups, which cost 1 us at T = 1 when few of
   // their wavefronts are idle). They wait on nothing, so no split row's exchange waits on them.
+  // The fields the prologue branches on or builds addresses from, fetched in one batch: left
+  // to itself the compiler loads each field at its first use, so every early branch (padding
+  // workgroups, XCD map, tokens past T) waited for a scalar load of its own, a chain of
+  // dependent round trips before the first vector load. The last field brings the struct's
+  // last 64-byte line into the scalar cache with the others, so the epilogue's loads of the
+  // remaining fields hit there.
+  asm volatile("" ::"s"(a.T), "s"(a.H), "s"(a.K), "s"(a.slices), "s"(a.xcd_map),
+               "s"(a.main_blocks), "s"(a.route_stride), "s"(a.scales_bf16), "s"(a.nv),
+               "s"(a.lanes), "s"(a.slot_span), "s"(a.slice_magic), "s"(a.idx), "s"(a.scales),
+               "s"(a.shared), "s"(a.residual), "s"(a.gamma), "s"(a.ws), "s"(a.split_quant));
   const int bid = blockIdx.x;
   if constexpr (MODE == MODE_NVFP4) {
     const int n_main = a.main_blocks;
@@ -241,20 +255,32 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   // they start together, instead of on consecutive XCDs, whose start times differ by up to
   // ~0.5 us that the exchange would wait for (the host's xcd_mapped chooses when). Workgroups
   // of tokens past T (T not a multiple of 8) exit at once.
+  // q / slices: one scalar multiply-high where the host found the reciprocal exact, instead of
+  // an integer division (a float reciprocal and some forty instructions before the first load).
+  const auto div_slices = [&](int q) -> int {
+    if (a.slices == 1) return q;
+    return a.slice_magic ? (int)__umulhi((uint32_t)q, a.slice_magic) : q / a.slices;
+  };
   int t, slice;
   if (a.xcd_map) {
     const int q = bid >> 3;
-    const int grp = q / a.slices;
+    const int grp = div_slices(q);
     slice = q - grp * a.slices;
     t = (grp << 3) + (bid & 7);
     if (t >= a.T) return;
   } else {
-    t = bid / a.slices;
+    t = div_slices(bid);
     slice = bid - t * a.slices;
   }
   const int tid = threadIdx.x;
   const int L = a.lanes;
-  const int g = __builtin_amdgcn_readfirstlane(tid / L);   // wave-uniform route group
+  // Wave-uniform route group. Groups are whole wavefronts, so scalar compares of the wavefront
+  // index replace a per-lane integer division that stood before the first load.
+  int g = 0;
+  if constexpr (G > 1) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lw = L >> 6;
+    g = (wave >= lw) + (G > 2 ? (wave >= 2 * lw) + (wave >= 3 * lw) : 0);
+  }
   const int lane = tid - g * L;
   const int slot0 = slice * a.slot_span;
   const uint32_t row_bytes = (uint32_t)a.H * 2;
@@ -330,6 +356,9 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
   // route's buffer is empty and reads zeros), then accumulate the present ones in float32 ----
   // exactly one of the two scale buffers is non-empty, the other reads zeros
   const uint32_t my_wbits = my_w32 | (my_w16 << 16);
+  // Rank sums (route_stride != 0) have an empty index buffer, which reads 0, and take row
+  // kk * route_stride + t: one formula for both, with no branch between the row loads.
+  const int t_rs = a.route_stride ? t : 0;
   constexpr int CH = JMAX < 16 / P ? JMAX : 16 / P;
   float acc[P][8];
 #pragma unroll
@@ -346,8 +375,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
     for (int jj = 0; jj < CH; ++jj) {
       const int k = g + (c0 + jj) * G;
       const int kk = k < a.K ? k : 0;
-      const int pidx =
-          a.route_stride ? kk * a.route_stride + t : __builtin_amdgcn_readlane((int)my_idx, kk);
+      const int pidx = __builtin_amdgcn_readlane((int)my_idx, kk) + kk * a.route_stride + t_rs;
       present[jj] = k < a.K && (uint32_t)pidx < (uint32_t)a.n_rows;
       const uint32_t wbits = (uint32_t)__builtin_amdgcn_readlane((int)my_wbits, kk);
       // an absent route's scale is never used: its weight is 0 (and its row reads zeros)
@@ -357,6 +385,9 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
 #pragma unroll
       for (int p = 0; p < P; ++p) v[jj][p] = __builtin_amdgcn_raw_buffer_load_b128(row_r, voff[p], 0, NT);
     }
+    // Every row load of the chunk is issued before the first use: without this barrier the
+    // scheduler may unpack an early route (and wait for it) between the later routes' loads.
+    __builtin_amdgcn_sched_barrier(0);
     // Every route is accumulated (an absent one adds 0 * 0): a use under a branch would let the
     // compiler sink the load into it and serialize the row loads.
 #pragma unroll
@@ -368,6 +399,9 @@ __global__ __launch_bounds__(1024) void finalize_kernel(const Params a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[p][e] = __builtin_fmaf(w[jj], x[e], acc[p][e]);
       }
+      // with 16 loads in a chunk, accumulate route by route so the unpacked values of later
+      // routes do not pile up in registers (that spilled)
+      if constexpr (CH * P > 8) __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -569,6 +603,8 @@ struct QuantParams {
 
 template <int ACT, int MODE>
 __global__ __launch_bounds__(64) void quantize_kernel(const QuantParams a) {
+  // the fields of the prologue in one batch of scalar loads, as in finalize_kernel
+  asm volatile("" ::"s"(a.T), "s"(a.slices), "s"(a.H), "s"(a.nv), "s"(a.x));
   if constexpr (MODE == MODE_NVFP4) {
     // the swizzled layout's padding rows are zeroed by workgroups of their own, in parallel
     // with the quantizing ones (one workgroup per token and slice is too few at decode sizes)
@@ -586,9 +622,11 @@ __global__ __launch_bounds__(64) void quantize_kernel(const QuantParams a) {
   const bool live = s < a.nv;
   const uint32_t voff = live ? (uint32_t)s * 16u : kOutOfRange;
   const uint32_t row_bytes = (uint32_t)a.H * 2u;
-  const double qs = (double)*a.qscale;
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc(a.x + (int64_t)t * row_bytes, row_bytes),
                                                         voff, 0, 0);
+  // the row load goes out before the scale's: nothing waits for the scale ahead of the row
+  __builtin_amdgcn_sched_barrier(0);
+  const double qs = (double)*a.qscale;
   float xr[8];
   Act<ACT>::unpack(v, xr);
   const uint32_t qrow = MODE == MODE_FP8 ? (uint32_t)a.H : (uint32_t)a.H / 2u;
@@ -923,6 +961,14 @@ static int check_pointers(const Common& c) {
   return MOE_FIN_OK;
 }
 
+// The reciprocal behind Params::slice_magic: m = ceil(2^32 / S) gives q / S = (q * m) >> 32 for
+// every q with q * S < 2^32 (the error q * (m - 2^32 / S) / 2^32 stays below 1 / S); 0 where
+// that does not hold for the workgroup indices below `grid` (the kernel divides then).
+static uint32_t slice_reciprocal(int64_t S, int64_t grid) {
+  if (S <= 1 || (uint64_t)grid * (uint64_t)S >= (1ull << 32)) return 0;
+  return (uint32_t)(((1ull << 32) + (uint64_t)S - 1) / (uint64_t)S);
+}
+
 static Params base_params(const Common& c) {
   Params p;
   memset(&p, 0, sizeof(p));
@@ -1039,6 +1085,7 @@ static int run_rows(int mode, const Common& c, const void* residual, const void*
   p.slot_span = cfg.span;
   p.slices = cfg.grid_x;
   p.main_blocks = (int)n_main;
+  p.slice_magic = slice_reciprocal(p.slices, n_main);
   p.xcd_map = xcd_mapped(mode, cfg) ? 1 : 0;
   p.ws = (uint8_t*)workspace;
   p.route_stride = route_stride;
@@ -1376,6 +1423,7 @@ int moe_finalize_run(const void* permuted_rows, int64_t num_permuted_rows,
   p.lanes = cfg.L;
   p.slot_span = cfg.span;
   p.slices = cfg.grid_x;
+  p.slice_magic = slice_reciprocal(p.slices, p.main_blocks);
   return to_code(dispatch<MODE_FIN>(act_dtype, p, cfg, (hipStream_t)stream));
 }
 

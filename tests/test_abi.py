@@ -425,3 +425,22 @@ def test_workspace_flag_validation_codes():
     assert f(A + 4, 0, ctypes.byref(v), None) == -5 and v.value == 5
     with pytest.raises(ValueError):
         M.moe_finalize_workspace_flag(torch.zeros(0, dtype=torch.uint8))
+
+
+def test_slice_reciprocal_is_exact_where_used():
+    """The kernel divides a workgroup index q by the slice count S as (q * m) >> 32 with
+    m = ceil(2^32 / S), and the host takes that form only where q * S < 2^32 for every index of
+    the grid. Check the claim exhaustively for the indices a split-row grid can have (S up to 16,
+    q below 2^20) and at the bound for every S a finalize-only grid can have (up to 2048)."""
+    import numpy as np
+
+    q = np.arange(1 << 20, dtype=np.uint64)
+    for S in range(2, 17):
+        m = np.uint64(((1 << 32) + S - 1) // S)
+        assert np.array_equal((q * m) >> np.uint64(32), q // np.uint64(S)), S
+    for S in range(2, 2049):
+        m = ((1 << 32) + S - 1) // S
+        top = ((1 << 32) - 1) // S                  # the largest q with q * S < 2^32
+        edge = [top - i for i in range(min(top, 3 * S) + 1)] + list(range(0, 3 * S))
+        # every residue class near the top, where the error term is largest
+        assert all((v * m) >> 32 == v // S for v in edge), S
