@@ -750,16 +750,21 @@ static int next_pow2(int x) {
 
 // Route groups of the row modes (same-run A/B on MI355X over top_k 1..22, T = 1..256): the
 // fewest groups that leave each group at most 4 routes (top_k 8: 2 groups of 4 routes beat 4
-// groups of 2 by 0.15 us at decode and 0.44 us at T = 32; top_k 16 and 22: 4 groups beat 2 by
-// 0.3-0.7 us), at least two wavefronts per workgroup when the routes allow it, and halved while
-// the groups span more than 512 lanes unless a group would then carry more than 8 routes
-// (T = 64, top_k 8: one group of 5 wavefronts beats two; top_k 16 or 22 keep two).
+// groups of 2 by 0.15 us at decode and 0.44 us at T = 32; top_k 16 and 22: 4 groups of one
+// wavefront beat 2 by 0.3-0.7 us), at least two wavefronts per workgroup when the routes allow
+// it, and halved while the groups span more than 256 lanes (split rows) or 512 (whole rows)
+// unless a group would then carry more than 8 routes. Split rows, forced group counts, same box:
+// top_k <= 8 with groups of 3-4 wavefronts (hidden 2560..7680 at decode, T = 48..64 at hidden
+// 5120..7168) run 0.09-0.13 us faster warm and 0.26-0.55 us faster cold as one group; top_k 10
+// and 16 with groups of 2 wavefronts 0.02 / 0.20-0.36 us faster as 2 groups than 4; groups of
+// 2 wavefronts at top_k 8 (the H6144 decode shapes) keep 2 groups, 0.15 us faster warm.
 static void finish_config(int K, Config* c) {
   int G = 1;
   while (G < 4 && 2 * G * c->L <= 1024 && 2 * G <= K &&
          ((K + G - 1) / G > 4 || G * c->L < 128))
     G *= 2;
-  while (G > 1 && G * c->L > 512 && (K + G / 2 - 1) / (G / 2) <= 8) G /= 2;
+  const int span_cap = c->grid_x > 1 ? 256 : 512;   // lanes of all groups, split / whole rows
+  while (G > 1 && G * c->L > span_cap && (K + G / 2 - 1) / (G / 2) <= 8) G /= 2;
   c->G = G;
   const int J = (K + G - 1) / G;
   c->JMAX = next_pow2(J < 4 ? 4 : J);
