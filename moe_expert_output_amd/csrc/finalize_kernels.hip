@@ -752,19 +752,30 @@ static int next_pow2(int x) {
 // fewest groups that leave each group at most 4 routes (top_k 8: 2 groups of 4 routes beat 4
 // groups of 2 by 0.15 us at decode and 0.44 us at T = 32; top_k 16 and 22: 4 groups of one
 // wavefront beat 2 by 0.3-0.7 us), at least two wavefronts per workgroup when the routes allow
-// it, and halved while the groups span more than 256 lanes (split rows) or 512 (whole rows)
-// unless a group would then carry more than 8 routes. Split rows, forced group counts, same box:
-// top_k <= 8 with groups of 3-4 wavefronts (hidden 2560..7680 at decode, T = 48..64 at hidden
-// 5120..7168) run 0.09-0.13 us faster warm and 0.26-0.55 us faster cold as one group; top_k 10
-// and 16 with groups of 2 wavefronts 0.02 / 0.20-0.36 us faster as 2 groups than 4; groups of
-// 2 wavefronts at top_k 8 (the H6144 decode shapes) keep 2 groups, 0.15 us faster warm.
-static void finish_config(int K, Config* c) {
+// it, and halved while the groups span more than 256 lanes unless a group would then carry more
+// routes than max_routes; whole rows from 1024 tokens take one group up to top_k 48. Forced
+// group counts, same box: split rows at top_k <= 8 with groups
+// of 3-4 wavefronts (hidden 2560..7680 at decode, T = 48..64 at hidden 5120..7168) run
+// 0.09-0.13 us faster warm and 0.26-0.55 us faster cold as one group; top_k 10 and 16 with
+// groups of 2 wavefronts 0.02 / 0.20-0.36 us faster as 2 groups than 4; groups of 2 wavefronts
+// at top_k 8 (the H6144 decode shapes, whole rows at hidden 1024) keep 2 groups, 0.10-0.15 us
+// faster warm. Whole rows, cold: one group wins at top_k <= 16 (T = 256: 0.18-0.33 us, T = 512
+// top_k 16: 1.4 us, T = 1024 top_k 16: 1.0-2.9 us), two at top_k 22 below 1024 tokens (T = 256 /
+// 512: 0.22 / 1.85 us faster than four), one from 1024 tokens (top_k 10 / 22 / 33 at hidden
+// 1024..2048: 3.1 / 4.0 / 5.3 us faster; top_k 64: 1.3 us faster at hidden 1024 but 2.1 us
+// slower at hidden 2560, so top_k above 48 keeps the halving rule).
+static void finish_config(int K, int64_t T, Config* c) {
   int G = 1;
   while (G < 4 && 2 * G * c->L <= 1024 && 2 * G <= K &&
          ((K + G - 1) / G > 4 || G * c->L < 128))
     G *= 2;
-  const int span_cap = c->grid_x > 1 ? 256 : 512;   // lanes of all groups, split / whole rows
-  while (G > 1 && G * c->L > span_cap && (K + G / 2 - 1) / (G / 2) <= 8) G /= 2;
+  if (c->grid_x == 1 && T >= 1024 && K <= 48) {
+    G = 1;    // whole rows, several workgroups per CU: they hide the chunks of a single group
+  } else {
+    // routes a group may carry after halving: split rows 8, whole rows 16 (one chunk of loads)
+    const int max_routes = c->grid_x > 1 ? 8 : 16;
+    while (G > 1 && G * c->L > 256 && (K + G / 2 - 1) / (G / 2) <= max_routes) G /= 2;
+  }
   c->G = G;
   const int J = (K + G - 1) / G;
   c->JMAX = next_pow2(J < 4 ? 4 : J);
@@ -847,13 +858,13 @@ static bool make_config(int mode, int64_t T, int H, int K, int slices, Config* c
     if (T >= 1024) {
       c->L = ((nv + c->P - 1) / c->P + 255) / 256 * 256;
       c->span = c->L * c->P;
-      finish_config(K, c);
+      finish_config(K, T, c);
       if (c->JMAX <= 8) return true;
     }
     c->L = ((nv + c->P - 1) / c->P + 63) / 64 * 64;
     c->span = c->L * c->P;
   }
-  finish_config(K, c);
+  finish_config(K, T, c);
   return true;
 }
 
