@@ -46,7 +46,7 @@ struct Params {
   // arrive in one batch of scalar loads (see the start of finalize_kernel).
   int T, H, K;
   int slices;                // workgroups per token (> 1: the row is split, see below)
-  int xcd_map;               // split rows: a token's slices share one XCD (see token_slice)
+  int xcd_map;               // split rows: a token's slices share one XCD (see the kernel)
   int main_blocks;           // workgroups before the scale-padding ones
   int route_stride;          // > 0: no route map; route k of token t is row k * route_stride + t
   int scales_bf16;
@@ -754,9 +754,9 @@ static int next_pow2(int x) {
 // wavefront beat 2 by 0.3-0.7 us), at least two wavefronts per workgroup when the routes allow
 // it, and halved while the groups span more than 256 lanes unless a group would then carry more
 // routes than max_routes; whole rows from 1024 tokens take one group up to top_k 48. Forced
-// group counts, same box: split rows at top_k <= 8 with groups
-// of 3-4 wavefronts (hidden 2560..7680 at decode, T = 48..64 at hidden 5120..7168) run
-// 0.09-0.13 us faster warm and 0.26-0.55 us faster cold as one group; top_k 10 and 16 with
+// group counts, same box: split rows at top_k <= 8 with groups of 3-4 wavefronts (hidden
+// 2560..7680 at decode, T = 48..64 at hidden 5120..7168) run 0.09-0.13 us faster warm and
+// 0.26-0.55 us faster cold as one group; top_k 10 and 16 with
 // groups of 2 wavefronts 0.02 / 0.20-0.36 us faster as 2 groups than 4; groups of 2 wavefronts
 // at top_k 8 (the H6144 decode shapes, whole rows at hidden 1024) keep 2 groups, 0.10-0.15 us
 // faster warm. Whole rows, cold: one group wins at top_k <= 16 (T = 256: 0.18-0.33 us, T = 512
