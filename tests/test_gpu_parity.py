@@ -448,6 +448,32 @@ def test_nvfp4(TH, layout):
     assert np.array_equal(qo2, qo) and np.array_equal(so2, so)
 
 
+@pytest.mark.parametrize("THK", [(1024, 2048, 22), (512, 2048, 22)])
+@pytest.mark.parametrize("qt", ["nvfp4", "fp8"])
+def test_quant_high_topk_whole_rows(THK, qt):
+    """Quantized outputs of whole rows with many routes per group (one group of 22 routes in two
+    chunks of loads from 1024 tokens, two groups of 11 below): codes and scales are the
+    quantization of the kernel's own rounded norm_out, bit for bit."""
+    T, H, K = THK
+    inp = make_inputs(T, H, K, seed=workload_seed("quant", T) + K)
+    _say(f"quant high top_k whole rows {qt} T={T} H={H} K={K}")
+    ref = oracle_ref(inp)
+    if qt == "nvfp4":
+        scale = O.nvfp4_global_scale(ref.N)
+        ro, no, qo, so = run_quant(inp, M.MOE_QUANT_NVFP4, scale, 1)
+    else:
+        scale = O.fp8_scale(ref.N)
+        ro, no, qo, so = run_quant(inp, M.MOE_QUANT_FP8_E4M3, scale, 1)
+    R, N = np64(ro), np64(no)
+    check_residual(R, ref, np64(inp.residual), "bf16")
+    check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")
+    if qt == "nvfp4":
+        own_c, own_s = O.quant_nvfp4(N, scale, 1)
+        assert np.array_equal(qo, own_c) and np.array_equal(so, own_s)
+    else:
+        assert np.array_equal(qo, O.quant_fp8(N, scale))
+
+
 @pytest.mark.parametrize("T,H", [(64, 6144), (3, 6144), (1030, 5120)])
 def test_fp8(T, H):
     inp = make_inputs(T, H, 8, seed=workload_seed("quant", T) + 7)
@@ -673,10 +699,14 @@ def test_quantize_nonfinite_bit_exact(act):
 # ---- large batches (prefill-sized calls: whole rows, nontemporal streaming) ---------------------
 @pytest.mark.parametrize("THK", [(256, 7168, 8), (512, 7168, 8), (2048, 2048, 8), (300, 3584, 16),
                                  (1024, 7168, 8), (1030, 5120, 8), (1024, 3584, 16),
-                                 (1024, 7168, 4), (1024, 7168, 16), (100, 16384, 4)])
+                                 (1024, 7168, 4), (1024, 7168, 16), (100, 16384, 4),
+                                 (1024, 1024, 10), (1024, 1024, 22), (1030, 1536, 33),
+                                 (512, 2048, 22)])
 def test_large_batch(THK):
     """From 1024 tokens whole-row workgroups are rounded up to four wavefronts (hidden 7168: 1024
-    lanes for 896 slots; 5120: 768 for 640), so their last lanes hold no slot."""
+    lanes for 896 slots; 5120: 768 for 640), so their last lanes hold no slot. From 1024 tokens
+    a whole row also takes a single route group up to top_k 48, so top_k 22 and 33 load their
+    routes in two and four chunks of 16; below that, top_k 22 runs as two groups of 11 routes."""
     T, H, K = THK
     full_check(make_inputs(T, H, K, seed=5000 + T + K))
 
