@@ -711,6 +711,14 @@ def test_large_batch(THK):
     full_check(make_inputs(T, H, K, seed=5000 + T + K))
 
 
+@pytest.mark.parametrize("THK", [(1024, 1024, 22), (512, 2048, 22), (1024, 7168, 8)])
+def test_large_batch_fp16_and_bf16_scales(THK):
+    """The same whole-row shapes with fp16 activations, and with bf16 routing weights."""
+    T, H, K = THK
+    full_check(make_inputs(T, H, K, seed=5100 + T + K, act_dtype="fp16"))
+    full_check(make_inputs(T, H, K, seed=5200 + T + K, scale_dtype="bf16"))
+
+
 def test_rows_beyond_4gib_sampled_tokens():
     """Maximum-size addressing: 17000 tokens at hidden 16384 and top_k 8 give 4.46 GB of permuted
     rows, so routes reach rows past the 4 GiB mark. The whole batch runs through the finalize and
