@@ -164,4 +164,72 @@ __device__ __forceinline__ uint32_t e2m1_code(float a, float gs, float sf) {
   return a == a ? above + 3u - below : 0u;
 }
 
+// gfx950 E2M1 conversion (v_cvt_scalef32_pk_fp4_f32) of N = 4 or 8 float32 values y[i] / hw,
+// packed 4 bits each, element i in bits 4i..4i+3. hw must be a power of two (the instruction
+// divides by 2^exponent(hw), exactly). Round to nearest even on the float32 input, saturating at
+// 6, sign kept; a NaN gives magnitude 7.
+template <int N>
+__device__ __forceinline__ uint32_t e2m1_cvt(const float* y, float hw) {
+  static_assert(N == 4 || N == 8, "four or eight elements");
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], hw, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], hw, 1);
+  if constexpr (N == 8) {
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], hw, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], hw, 3);
+  }
+  return w;
+}
+
+// The inverse (v_cvt_scalef32_pk_f32_fp4, scale 1): the values of the N codes packed in w.
+template <int N>
+__device__ __forceinline__ void e2m1_values(uint32_t w, float v[N]) {
+  const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 0);
+  const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 1);
+  v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+  if constexpr (N == 8) {
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 2);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.f, 3);
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
+  }
+}
+
+// E2M1 codes (sign and magnitude, packed as by e2m1_cvt) of x[i] * gs / sf rounded to nearest
+// even exactly, for an E4M3 block scale sf (0 gives the signed zeros of the x[i]) and a global
+// scale gs in [2^-100, 2^100]; x[i] are bf16 or fp16 values, not NaN.
+// 1. q = gs * rcp(sf) is within three float32 roundings of gs / sf, so the hardware codes of
+//    x * q (1 - 2^-19) and x * q (1 + 2^-19) bracket the exact code: equal, or c and c + 1
+//    when x * gs / sf lies within ~2^-18 of the midpoint m between them (or on it).
+// 2. From the two codes' values, S = 2m in the bracketed case and S = 2 * value otherwise, and
+//    d = fma(|x|, gs, -(S / 2) * sf), whose sign is the exact sign of x * gs - m * sf (the same
+//    argument as for e2m1_code: (S / 2) * sf is exact and the difference cannot underflow).
+// 3. S + clamp(d * 2^17 / sf, +-2^-5), divided by 2 in the conversion, is m moved off the
+//    midpoint by at least two float32 steps in the exact direction (a nonzero |x * gs - m * sf|
+//    is at least 2^-36 of m * sf: x * gs has at most 35 significant bits), or m itself on a
+//    tie, which the conversion then rounds to even; away from midpoints it stays within 2^-6
+//    of the value, inside that code's interval. About 10 operations per element, no branch.
+template <int N>
+__device__ __forceinline__ uint32_t e2m1_pack_exact(const float* x, float gs, float sf) {
+  const float r = sf != 0.f ? __builtin_amdgcn_rcpf(sf) : 0.f;
+  const float q = gs * r, q_lo = q * (1.f - 0x1p-19f), q_hi = q * (1.f + 0x1p-19f);
+  float y[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) y[i] = x[i] * q_lo;
+  const uint32_t w_lo = e2m1_cvt<N>(y, 1.f);
+#pragma unroll
+  for (int i = 0; i < N; ++i) y[i] = x[i] * q_hi;
+  const uint32_t w_hi = e2m1_cvt<N>(y, 1.f);
+  float v_lo[N], v_hi[N];
+  e2m1_values<N>(w_lo & 0x77777777u, v_lo);
+  e2m1_values<N>(w_hi & 0x77777777u, v_hi);
+  const float hsf = 0.5f * sf, k2 = 0x1p17f * r, bd = 0x1p-22f * sf;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const float s2 = v_lo[i] + v_hi[i];
+    const float d = __builtin_fmaf(__builtin_fabsf(x[i]), gs, -(s2 * hsf));
+    y[i] = __builtin_fmaf(__builtin_amdgcn_fmed3f(d, -bd, bd), k2, s2);
+  }
+  return (e2m1_cvt<N>(y, 2.f) & 0x77777777u) | (w_lo & 0x88888888u);
+}
+
 }  // namespace mfin

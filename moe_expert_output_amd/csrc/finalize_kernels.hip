@@ -162,12 +162,19 @@ __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
     // a zero block scale gives signed zero codes; a NaN block gives zero codes without signs
     const uint32_t keep = sfc != 0 && !nan_blk ? 7u : 0u;
     const uint32_t sign_keep = nan_blk ? 0u : 1u;
+    // The exact branch-free encoder for the usual range of global scales; the per-midpoint
+    // tests of e2m1_code beyond it (a uniform branch: gs is the same for every lane).
     uint32_t word = 0;
+    if (gs >= 0x1p-100f && gs <= 0x1p100f) {
+      word = e2m1_pack_exact<E1 - E0>(nr + E0, gs, sf);
+    } else {
 #pragma unroll
-    for (int e = E0; e < E1; ++e) {
-      const uint32_t m = e2m1_code(__builtin_fabsf(nr[e]), gs, sf) & keep;
-      word |= (m | ((sign_bit(nr[e]) & sign_keep) << 3)) << (4 * (e - E0));
+      for (int e = E0; e < E1; ++e) {
+        const uint32_t m = e2m1_code(__builtin_fabsf(nr[e]), gs, sf) & keep;
+        word |= (m | ((sign_bit(nr[e]) & sign_keep) << 3)) << (4 * (e - E0));
+      }
     }
+    word = nan_blk ? 0u : word;
     if constexpr (HALF == 0) {
       __builtin_amdgcn_raw_buffer_store_b32(word, q_r, voff >> 2, 0, 0);
     } else {

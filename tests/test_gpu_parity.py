@@ -658,6 +658,76 @@ def test_quantize_near_midpoints_bit_exact(act):
         assert np.array_equal(got_c, want_c) and np.array_equal(got_s, want_s), ("scale", draw)
 
 
+def _format_values_between(lo, hi, act):
+    """Every positive bf16 / fp16 value in [lo, hi] (bit patterns of positive values are ordered)."""
+    fmt = O.BF16 if act == "bf16" else O.FP16
+    a, b = (int(O.encode_bits(_act_vals([v], act), fmt)[0]) for v in (lo, hi))
+    return O.decode_bits(np.arange(a, b + 1, dtype=np.uint16), fmt)
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp16"])
+def test_quantize_nvfp4_value_sweep_bit_exact(act):
+    """Every bf16 / fp16 value from 1/64 of a block's maximum up to it, in blocks whose scales
+    take every E4M3 significand, under global scales of three kinds: small integers, float32
+    quotients 2688 / amax as a tensor-wide maximum gives them, and random float32 values. This
+    puts elements on and next to all seven E2M1 rounding midpoints (exact ties and float32 near
+    ties), where the encoder's bracketing conversion hands over to its exact midpoint test."""
+    rng = np.random.default_rng(4242 if act == "bf16" else 4243)
+    gss = [100.0, 6.0, float(np.float32(2688.0 / float(_act_vals([3.40625], act)[0]))),
+           float(np.float32(2688.0 / float(_act_vals([0.71875], act)[0]))),
+           float(np.float32(rng.uniform(10, 1000)))]
+    H = 2048
+    for gs in gss:
+        blocks = []
+        for sig in range(8, 16):
+            sf_target = sig / 8.0 * 2.0 ** int(rng.integers(-3, 4))
+            amax = float(_act_vals([6.0 * sf_target / gs], act)[0])
+            vals = _format_values_between(amax / 64, amax, act)
+            vals = vals[vals < amax]
+            vals = vals * rng.choice([-1.0, 1.0], size=len(vals))
+            for i in range(0, len(vals), 15):
+                blk = np.zeros(16)
+                blk[0] = amax if i % 2 else -amax
+                chunk = vals[i:i + 15]
+                blk[1:1 + len(chunk)] = chunk
+                blocks.append(blk)
+        nb = H // 16
+        n_rows = -(-len(blocks) // nb)
+        N = np.zeros((n_rows * nb, 16))
+        N[:len(blocks)] = np.array(blocks)
+        N = N.reshape(n_rows, H)
+        for layout in (M.MOE_SF_SWIZZLED_128x4, M.MOE_SF_LINEAR):
+            want_c, want_s = O.quant_nvfp4(N, gs, layout)
+            got_c, got_s = _quantize_dev(N, act, M.MOE_QUANT_NVFP4, gs, layout)
+            assert np.array_equal(got_s, want_s), (gs, layout)
+            assert np.array_equal(got_c, want_c), (gs, layout)
+
+
+@pytest.mark.parametrize("k", [-110, 0, 110])
+def test_quantize_nvfp4_extreme_global_scales(k):
+    """The E2M1 midpoint row of test_quantize_rounding_midpoints_bit_exact scaled by 2^k with the
+    global scale 2^-k: the same codes and block scales. Global scales outside [2^-100, 2^100]
+    take the encoder's per-midpoint tests instead of its bracketing conversion."""
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    vals = []
+    for m in mids:
+        b = O.round_to_format(np.array([m]), O.BF16)[0]
+        vals += [b, O.round_to_format(np.array([b * (1 + 2 ** -7)]), O.BF16)[0],
+                 O.round_to_format(np.array([b * (1 - 2 ** -8)]), O.BF16)[0], -b]
+    row = np.zeros(64)
+    for i in range(4):
+        row[16 * i] = 6.0
+        chunk = vals[7 * i:7 * i + 7]
+        row[16 * i + 1:16 * i + 1 + len(chunk)] = chunk
+    N0 = np.stack([row, row * 2.0 ** -5])
+    want_c, want_s = O.quant_nvfp4(N0, 1.0, 1)
+    N = N0 * 2.0 ** k                        # exact: powers of two within bf16's range
+    gs = 2.0 ** -k
+    got_c, got_s = _quantize_dev(N, "bf16", M.MOE_QUANT_NVFP4, gs, 1)
+    assert np.array_equal(O.quant_nvfp4(N, gs, 1)[0], want_c)
+    assert np.array_equal(got_c, want_c) and np.array_equal(got_s, want_s)
+
+
 @pytest.mark.parametrize("act", ["bf16", "fp16"])
 def test_quantize_nonfinite_bit_exact(act):
     """Infinities saturate (E4M3 448, E2M1 6); a NaN of either sign gives FP8 code 0x7F, and a
