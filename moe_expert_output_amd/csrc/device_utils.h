@@ -105,10 +105,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // Maximum of v and the value of lane ^ 1 (the other half of a 16-element NVFP4 block).
-__device__ __forceinline__ float pair_max(float v) {
-  float o = __builtin_bit_cast(
-      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-  return fmaxf(v, o);
+__device__ __forceinline__ uint32_t pair_max_u32(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+  return max(v, o);
 }
 
 // --- exact-decision narrow encoders ------------------------------------------------------------
@@ -162,6 +161,33 @@ __device__ __forceinline__ uint32_t e2m1_code(float a, float gs, float sf) {
                          sign_bit(__builtin_fmaf(a, gs, -1.75f * sf)) +
                          sign_bit(__builtin_fmaf(a, gs, -3.5f * sf));
   return a == a ? above + 3u - below : 0u;
+}
+
+// The value of E4M3 code c (gfx950 v_cvt_f32_fp8, OCP E4M3; code 0x7F gives NaN).
+__device__ __forceinline__ float e4m3_value_hw(uint32_t c) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
+}
+
+// E4M3 code of amax * gs / 6 rounded to nearest even exactly, saturating at 448 (0x7E), for a
+// block maximum amax >= 0 (a bf16 / fp16 magnitude or infinity, not NaN) and gs in
+// [2^-100, 2^100]. The same three steps as e2m1_pack_exact on the E4M3 grid (gfx950
+// v_cvt_pk_fp8_f32: round to nearest even on the float32 input; it gives NaN from 464 up, so
+// inputs are clamped to 448 first): the codes of v (1 -+ 2^-19), v = amax * (gs * (1/6))
+// within three float32 roundings of amax * gs / 6, bracket the exact one; S = 2m from their
+// values (a midpoint m, or twice a value); the exact sign of amax * gs - 3S from one FMA
+// (3S is exact, and amax * gs has at most 35 significant bits); S moved by
+// clamp(d * 2^16, +-S * 2^-6), halved, then converted. A cell of the E4M3 grid is at least
+// 1/15 of its value wide, so the +-2^-6 move stays inside it.
+__device__ __forceinline__ uint32_t e4m3_block_scale_exact(float amax, float gs) {
+  const float v = amax * (gs * (1.f / 6.f));
+  const float v_lo = fminf(v * (1.f - 0x1p-19f), 448.f), v_hi = fminf(v * (1.f + 0x1p-19f), 448.f);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v_lo, v_hi, 0, false);
+  const auto s = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+  const float s2 = s[0] + s[1];
+  const float d = __builtin_fmaf(amax, gs, -3.f * s2);
+  const float bd = 0x1p-22f * s2;
+  const float y = 0.5f * __builtin_fmaf(__builtin_amdgcn_fmed3f(d, -bd, bd), 0x1p16f, s2);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xFFu;
 }
 
 // gfx950 E2M1 conversion (v_cvt_scalef32_pk_fp4_f32) of N = 4 or 8 float32 values y[i] / hw,

@@ -148,30 +148,32 @@ __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
   } else {
     // NVFP4: a 16-element block is this lane's 8 elements and the neighbouring lane's 8.
     // A NaN anywhere in the block makes its amax NaN: scale code 0x7F and all-zero codes.
-    float amax = 0.f, nan_here = 0.f;
+    // Magnitude bit patterns order like the magnitudes, with NaN above infinity, so one
+    // unsigned maximum gives both the block amax and the NaN test.
+    uint32_t amax_bits = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      amax = fmaxf(amax, __builtin_fabsf(nr[e]));
-      nan_here = nr[e] == nr[e] ? nan_here : 1.f;
-    }
-    amax = pair_max(amax);
-    const bool nan_blk = pair_max(nan_here) != 0.f;
-    const uint32_t sfc = nan_blk ? 0x7Fu : e4m3_code((double)amax * qs / 6.0);
-    const float sf = (float)e4m3_value(sfc);    // exact: an E4M3 value
+    for (int e = 0; e < 8; ++e)
+      amax_bits = max(amax_bits, __builtin_bit_cast(uint32_t, nr[e]) & 0x7FFFFFFFu);
+    amax_bits = pair_max_u32(amax_bits);
+    const bool nan_blk = amax_bits > 0x7F800000u;
+    const float amax = __builtin_bit_cast(float, amax_bits);
     const float gs = (float)qs;                 // exact: the caller's float32 scale
-    // a zero block scale gives signed zero codes; a NaN block gives zero codes without signs
-    const uint32_t keep = sfc != 0 && !nan_blk ? 7u : 0u;
-    const uint32_t sign_keep = nan_blk ? 0u : 1u;
-    // The exact branch-free encoder for the usual range of global scales; the per-midpoint
-    // tests of e2m1_code beyond it (a uniform branch: gs is the same for every lane).
-    uint32_t word = 0;
+    uint32_t sfc, word = 0;
     if (gs >= 0x1p-100f && gs <= 0x1p100f) {
-      word = e2m1_pack_exact<E1 - E0>(nr + E0, gs, sf);
+      // the branch-free exact encoders for the usual range of global scales (a uniform
+      // branch: gs is the same for every lane)
+      sfc = nan_blk ? 0x7Fu : e4m3_block_scale_exact(amax, gs);
+      word = e2m1_pack_exact<E1 - E0>(nr + E0, gs, e4m3_value_hw(sfc));
     } else {
+      // beyond it, float64 for the block scale and per-midpoint tests for the codes
+      sfc = nan_blk ? 0x7Fu : e4m3_code((double)amax * qs / 6.0);
+      const float sf = (float)e4m3_value(sfc);  // exact: an E4M3 value
+      // a zero block scale gives signed zero codes (a NaN block is cleared below)
+      const uint32_t keep = sfc != 0 ? 7u : 0u;
 #pragma unroll
       for (int e = E0; e < E1; ++e) {
         const uint32_t m = e2m1_code(__builtin_fabsf(nr[e]), gs, sf) & keep;
-        word |= (m | ((sign_bit(nr[e]) & sign_keep) << 3)) << (4 * (e - E0));
+        word |= (m | (sign_bit(nr[e]) << 3)) << (4 * (e - E0));
       }
     }
     word = nan_blk ? 0u : word;
