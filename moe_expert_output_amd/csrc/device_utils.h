@@ -190,6 +190,37 @@ __device__ __forceinline__ uint32_t e4m3_block_scale_exact(float amax, float gs)
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y, 0.f, 0, false) & 0xFFu;
 }
 
+// OCP E4M3 codes of x[i] * s8 (i < 8, byte i of the pair of words) rounded to nearest even
+// exactly, saturating at 448 (0x7E); a NaN gives 0x7F whatever its sign. The float32 product p
+// is made round-to-odd (p one step toward zero when the exact FMA residual is negative, then
+// the last bit set when it is nonzero), which keeps every rounding decision to the 4-bit E4M3
+// significand (22 spare bits: Boldo and Melquiond's round-to-odd result); gfx950
+// v_cvt_pk_fp8_f32 then rounds it to nearest even. Products above 448 (infinities included)
+// are clamped first, since the conversion gives NaN from 464 up; a NaN code's sign bit is
+// cleared in the packed words.
+__device__ __forceinline__ u32x2 e4m3_pack8_exact(const float x[8], float s8) {
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float a = __builtin_fabsf(x[i]);
+    const float p = a * s8;
+    const uint32_t rb = __builtin_bit_cast(uint32_t, __builtin_fmaf(a, s8, -p));
+    const uint32_t t = (__builtin_bit_cast(uint32_t, p) - (rb >> 31)) | min(rb, 1u);
+    const float m = p > 448.f ? 448.f : __builtin_bit_cast(float, t);   // a NaN stays NaN
+    y[i] = __builtin_copysignf(m, x[i]);
+  }
+  u32x2 w;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * j], y[4 * j + 1], 0, false);
+    v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4 * j + 2], y[4 * j + 3], (int)v, true);
+    // bytes whose magnitude is 0x7F (NaN; finite codes stop at 0x7E) lose their sign bit
+    const uint32_t nan_bytes = ((v & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    w[j] = v & ~nan_bytes;
+  }
+  return w;
+}
+
 // gfx950 E2M1 conversion (v_cvt_scalef32_pk_fp4_f32) of N = 4 or 8 float32 values y[i] / hw,
 // packed 4 bits each, element i in bits 4i..4i+3. hw must be a power of two (the instruction
 // divides by 2^exponent(hw), exactly). Round to nearest even on the float32 input, saturating at

@@ -136,14 +136,7 @@ __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
   static_assert(HALF == 0 || MODE == MODE_NVFP4, "only the NVFP4 codes are split");
   constexpr int E0 = HALF == 2 ? 4 : 0, E1 = HALF == 1 ? 4 : 8;
   if constexpr (MODE == MODE_FP8) {
-    u32x2 q = {0u, 0u};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      // a NaN encodes as 0x7F whatever its sign bit
-      const uint32_t sgn = nr[e] == nr[e] ? sign_bit(nr[e]) : 0u;
-      const uint32_t c = e4m3_code(__builtin_fabs((double)nr[e]) * qs) | (sgn << 7);
-      q[e >> 2] |= c << (8 * (e & 3));
-    }
+    const u32x2 q = e4m3_pack8_exact(nr, (float)qs);   // exact: the caller's float32 scale
     __builtin_amdgcn_raw_buffer_store_b64(q, q_r, voff >> 1, 0, NTQ);
   } else {
     // NVFP4: a 16-element block is this lane's 8 elements and the neighbouring lane's 8.
