@@ -110,6 +110,14 @@ __device__ __forceinline__ uint32_t pair_max_u32(uint32_t v) {
   return max(v, o);
 }
 
+// The value of lane + N within the lane's row of 16 (DPP row_shl:N, one VALU operation instead
+// of an LDS permute); lanes whose lane + N leaves the row get 0.
+template <int N>
+__device__ __forceinline__ uint32_t row_shl_dpp(uint32_t v) {
+  static_assert(N >= 1 && N <= 15, "row shift");
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 + N, 0xF, 0xF, false);
+}
+
 // --- exact-decision narrow encoders ------------------------------------------------------------
 // Branch-free: every lane runs the same instruction stream, so the codes of a lane's 8 elements
 // are independent chains the compiler can interleave.

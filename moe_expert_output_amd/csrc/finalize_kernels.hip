@@ -179,9 +179,11 @@ __device__ __forceinline__ void quantize_store(const float nr[8], double qs,
     }
     // Scale bytes: lanes 8m..8m+7 hold blocks 4m'..4m'+3 (two lanes per block).
     const uint32_t sf_here = live ? sfc : 0u;
-    const uint32_t b1 = __shfl_down(sf_here, 2, 64);
-    const uint32_t b2 = __shfl_down(sf_here, 4, 64);
-    const uint32_t b3 = __shfl_down(sf_here, 6, 64);
+    // (a workgroup's slot span is a multiple of 8, so the storing lanes are lanes 8m and read
+    // lanes 8m + 2, 4, 6 of their own 16-lane row)
+    const uint32_t b1 = row_shl_dpp<2>(sf_here);
+    const uint32_t b2 = row_shl_dpp<4>(sf_here);
+    const uint32_t b3 = row_shl_dpp<6>(sf_here);
     if (live && (s & 7) == 0) {
       const int b = s >> 1;                      // first block of the group of four
       const int nb = d.H >> 4;
