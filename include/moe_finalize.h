@@ -196,8 +196,9 @@ int moe_finalize_workspace_flag(const void* workspace, int clear, int* flag, voi
  *                FP8 scale s8. NVFP4: for every 16-element block of a row, sf = E4M3(gs*amax/6)
  *                and codes q = E2M1(x*gs/sf) (signed zeros when sf == 0). FP8: q = E4M3(x*s8).
  *                All conversions round to nearest even and saturate (E4M3 at 448, E2M1 at 6;
- *                infinities saturate too); the rounding decisions are exact (made in float64,
- *                where x*gs is exact). Non-finite values: an FP8 NaN is 0x7F whatever its
+ *                infinities saturate too); every code equals the rounding of the exact real
+ *                product or quotient, not of a float32 approximation of it, ties included.
+ *                Non-finite values: an FP8 NaN is 0x7F whatever its
  *                sign; an NVFP4 block holding a NaN gets scale code 0x7F and all codes 0.
  *   quant_out    NVFP4: [num_tokens, hidden/2] bytes, element 2j in the low nibble of byte j.
  *                FP8:   [num_tokens, hidden] bytes.
