@@ -6,6 +6,7 @@ invariant the pages fix, or a number the pages print. Runs on the CPU (no GPU ma
 from __future__ import annotations
 
 import math
+import os
 from fractions import Fraction
 
 import numpy as np
@@ -309,11 +310,24 @@ def tp4_errors(H, T, W=4, seed0=0):
     return floor, np.abs(new - ref_res).mean(), np.abs(old - ref_res).mean()
 
 
+def _golden_ranges(name):
+    """quantity -> (low, high) from a fixture under tests/golden/ (whitespace columns, # comments)."""
+    out = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].split()
+            if line:
+                out[line[0]] = (float(line[1]), float(line[2]))
+    return out
+
+
 def test_pages_tp4_accuracy_figures():
+    want = _golden_ranges("tp4_accuracy.txt")
     floor, new, old = tp4_errors(6144, 32)
-    assert 4.7e-3 <= floor <= 4.95e-3, floor
-    assert 5.85e-3 <= new <= 6.15e-3, new
-    assert 7.6e-3 <= old <= 8.0e-3, old
+    for name, got in (("bf16_rounding_floor", floor), ("fp32_accumulation_rounded_once", new),
+                      ("per_step_rounding", old)):
+        lo, hi = want[name]
+        assert lo <= got <= hi, (name, got)
 
 
 # ------------------------------------------------------------------------------------------------
