@@ -193,7 +193,10 @@ int moe_finalize_workspace_flag(const void* workspace, int clear, int* flag, voi
  *
  *   quant_type   MOE_QUANT_NVFP4 or MOE_QUANT_FP8_E4M3.
  *   quant_scale  device pointer to ONE float32: the per-tensor global scale gs (NVFP4) or the
- *                FP8 scale s8. NVFP4: for every 16-element block of a row, sf = E4M3(gs*amax/6)
+ *                FP8 scale s8, positive and finite (as the pages' per-tensor scales 448*6/amax
+ *                and 448/amax are; it is read on the device, so it is not checked: for a zero,
+ *                negative or non-finite scale the codes are not specified, and the call still
+ *                completes without touching memory outside its outputs). NVFP4: for every 16-element block of a row, sf = E4M3(gs*amax/6)
  *                and codes q = E2M1(x*gs/sf) (signed zeros when sf == 0). FP8: q = E4M3(x*s8).
  *                All conversions round to nearest even and saturate (E4M3 at 448, E2M1 at 6;
  *                infinities saturate too); every code equals the rounding of the exact real
