@@ -836,6 +836,14 @@ static bool make_config(int mode, int64_t T, int H, int K, int slices, Config* c
     const int64_t waves = (T > 0 ? T : 1) * c->grid_x;
     int G = 1;
     while (G < 4 && (K + G - 1) / G > 4 && waves * 2 * G <= 2048) G *= 2;
+    // Past the wavefront cap, one group of 17..24 routes loads its rows in two chunks; four
+    // groups of at most 6 were as fast or faster at every measured size (cold, T = 64..1000,
+    // hidden 4096..16384; top_k 17: T=100 H7168 7.76 -> 6.55 us, T=250 H4096 8.83 -> 7.73;
+    // top_k 22: T=100 H16384 13.63 -> 12.28; top_k 24: T=1000 H16384 119.3 -> 117.7; worst
+    // case top_k 17 T=1000 H16384 91.82 -> 91.96). top_k 25..32 (7-8 routes a group) measured
+    // mixed (+0.1..0.2 us at T <= 250, -1.3..-3.5 us at T = 1000) and top_k 33 lost up to
+    // 10 us at T = 1000, so both keep the cap.
+    if ((K + G - 1) / G > 16 && K <= 24) G = 4;
     c->G = G;
     const int J = (K + G - 1) / G;
     c->JMAX = next_pow2(J < 4 ? 4 : J);

@@ -467,6 +467,11 @@ MEASURED_BEST = [
     (1, 4, 1024, 8, 1, 2, "2 groups 2.95 warm vs 1: 3.06"),
     (2, 64, 6144, 8, 4, 1, "NVFP4: 4 slices, 1 group 5.32 cold vs 2 groups 5.88"),
     (2, 1, 6144, 8, 6, 2, "NVFP4: 2 groups 4.15 warm vs 1: 4.35"),
+    (0, 100, 7168, 17, 1, 4, "finalize: 4 groups 6.55 cold vs 1: 7.76"),
+    (0, 100, 16384, 22, 1, 4, "finalize: 4 groups 12.28 cold vs 1: 13.45, 2: 12.68"),
+    (0, 250, 7168, 22, 1, 4, "finalize: 4 groups 13.27 cold vs 1: 13.94"),
+    (0, 250, 7168, 32, 1, 1, "finalize: 1 group 17.47 cold vs 4: 17.60"),
+    (0, 1000, 7168, 33, 1, 1, "finalize: 1 group 68.3 cold vs 4: 71.5"),
 ]
 
 

@@ -130,6 +130,17 @@ def test_high_topk(T, sdt, HK):
                            seed=workload_seed("highk", T, "bf16", sdt, K)), config="high_topk")
 
 
+@pytest.mark.parametrize("THKG", [(100, 7168, 17, 4), (300, 2048, 22, 4), (512, 4096, 24, 4),
+                                  (250, 7168, 32, 1)])
+def test_finalize_mid_batch_high_topk(THKG):
+    """Finalize-only past the route-group wavefront cap: top_k 17..24 in four route groups,
+    top_k 32 in one, against the oracle's admissible window."""
+    T, H, K, G = THKG
+    assert M.moe_finalize_launch_config(0, T, H, K, num_cus=256)["route_groups"] == G
+    full_check(make_inputs(T, H, K, seed=workload_seed("highk", T, "bf16", "fp32", K) + H),
+               rmsnorm=False)
+
+
 # ---- exactness: indices, route selection, poison -------------------------------------------------
 @pytest.mark.parametrize("act", ["bf16", "fp16"])
 def test_k1_exact_gather(act):
