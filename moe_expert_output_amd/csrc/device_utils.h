@@ -202,7 +202,8 @@ __device__ __forceinline__ uint32_t e4m3_block_scale_exact(float amax, float gs)
 // exactly, saturating at 448 (0x7E); a NaN gives 0x7F whatever its sign. The float32 product p
 // is made round-to-odd (p one step toward zero when the exact FMA residual is negative, then
 // the last bit set when it is nonzero), which keeps every rounding decision to the 4-bit E4M3
-// significand (22 spare bits: Boldo and Melquiond's round-to-odd result); gfx950
+// significand (round-to-odd at 24 bits followed by a rounding to at most 22 is a single correct
+// rounding: Boldo and Melquiond's result); gfx950
 // v_cvt_pk_fp8_f32 then rounds it to nearest even. Products above 448 (infinities included)
 // are clamped first, since the conversion gives NaN from 464 up; a NaN code's sign bit is
 // cleared in the packed words.
@@ -272,7 +273,7 @@ __device__ __forceinline__ void e2m1_values(uint32_t w, float v[N]) {
 //    midpoint by at least two float32 steps in the exact direction (a nonzero |x * gs - m * sf|
 //    is at least 2^-36 of m * sf: x * gs has at most 35 significant bits), or m itself on a
 //    tie, which the conversion then rounds to even; away from midpoints it stays within 2^-6
-//    of the value, inside that code's interval. About 10 operations per element, no branch.
+//    of the value, inside that code's interval. About 12 instructions per element, no branch.
 template <int N>
 __device__ __forceinline__ uint32_t e2m1_pack_exact(const float* x, float gs, float sf) {
   const float r = sf != 0.f ? __builtin_amdgcn_rcpf(sf) : 0.f;
