@@ -485,6 +485,33 @@ def test_quant_high_topk_whole_rows(THK, qt):
         assert np.array_equal(qo, O.quant_fp8(N, scale))
 
 
+@pytest.mark.parametrize("use_ws", [True, False])
+@pytest.mark.parametrize("TH", [(3, 16384), (260, 12288)])
+@pytest.mark.parametrize("qt", ["nvfp4", "fp8"])
+def test_quant_wide_rows(TH, qt, use_ws):
+    """Rows wider than 8192: whole-row workgroups hold two slots per lane, and split rows many
+    slices; codes and scales are the quantization of the kernel's own rounded norm_out, bit for
+    bit, in both row modes."""
+    T, H = TH
+    inp = make_inputs(T, H, 8, seed=workload_seed("quant", T) + H + 3)
+    _say(f"quant wide rows {qt} T={T} H={H} use_ws={use_ws}")
+    ref = oracle_ref(inp)
+    if qt == "nvfp4":
+        scale = O.nvfp4_global_scale(ref.N)
+        ro, no, qo, so = run_quant(inp, M.MOE_QUANT_NVFP4, scale, 1, use_ws=use_ws)
+    else:
+        scale = O.fp8_scale(ref.N)
+        ro, no, qo, so = run_quant(inp, M.MOE_QUANT_FP8_E4M3, scale, 1, use_ws=use_ws)
+    R, N = np64(ro), np64(no)
+    check_residual(R, ref, np64(inp.residual), "bf16")
+    check_norm(N, R, ref, np64(inp.gamma), inp.eps, "bf16")
+    if qt == "nvfp4":
+        own_c, own_s = O.quant_nvfp4(N, scale, 1)
+        assert np.array_equal(qo, own_c) and np.array_equal(so, own_s)
+    else:
+        assert np.array_equal(qo, O.quant_fp8(N, scale))
+
+
 @pytest.mark.parametrize("T,H", [(64, 6144), (3, 6144), (1030, 5120)])
 def test_fp8(T, H):
     inp = make_inputs(T, H, 8, seed=workload_seed("quant", T) + 7)
