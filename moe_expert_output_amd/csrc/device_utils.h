@@ -1,5 +1,6 @@
 // device_utils.h -- gfx950 device helpers of the MoE finalize kernels: 128-bit activation
-// packing, wavefront reductions over DPP, and exact-decision FP8/FP4 encoders.
+// packing, wavefront reductions over DPP, and exact FP8/FP4 encoders (software ones and ones
+// built on the gfx950 conversion instructions).
 //
 // Sources (cited by key): [FI6631] flashinfer PR #6631 "perf(comm): gather MoE-finalize routes
 // together and accumulate in FP32"; [FI3385] flashinfer PR #3385 "feat: MNNVL Allreduce quant
@@ -120,7 +121,10 @@ __device__ __forceinline__ uint32_t row_shl_dpp(uint32_t v) {
 
 // --- exact-decision narrow encoders ------------------------------------------------------------
 // Branch-free: every lane runs the same instruction stream, so the codes of a lane's 8 elements
-// are independent chains the compiler can interleave.
+// are independent chains the compiler can interleave. e4m3_code, e4m3_value and e2m1_code are
+// the software encoders (float64 and per-midpoint FMA tests); the kernels use them only for
+// NVFP4 global scales outside [2^-100, 2^100]. The hardware-conversion encoders further down
+// (e4m3_block_scale_exact, e4m3_pack8_exact, e2m1_pack_exact) serve every other call.
 //
 // OCP E4M3 ("fn") of an exact float64 magnitude y: bias 7, 3 mantissa bits, subnormals m * 2^-9,
 // max 448. Round to nearest even, saturate at 448. y >= 0, finite, infinite or NaN. Returns the

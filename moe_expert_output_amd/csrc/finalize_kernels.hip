@@ -26,7 +26,8 @@
 // through LDS, which adds them in group order (deterministic). Group 0 applies the routed
 // scaling and shared add, rounds once, adds the residual, and reduces the sum of squares with a
 // DPP wavefront reduction plus one LDS pass across wavefronts. Quantized outputs are encoded
-// with exact rounding decisions (E4M3 in float64, E2M1 as exact signs of float32 FMAs).
+// with gfx950's FP4/FP8 conversion instructions, made exact (the code of the exact product or
+// quotient, ties included) by the steps described at the encoders in device_utils.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
