@@ -16,7 +16,7 @@ from tests import test_oracle_quant_pins as Q
 
 _orig = {name: getattr(R, name) for name in
          ("finalize_unrounded", "round_to_format", "residual_rmsnorm", "quant_nvfp4",
-          "sf_offset", "reference_unrounded", "finalize_magnitude")}
+          "quant_fp8", "sf_offset", "reference_unrounded", "finalize_magnitude")}
 
 
 def _fin_no_rsf(rows, idx, scales, shared, rsf):
@@ -80,6 +80,59 @@ def _nvfp4_nibbles_swapped(N, gs, layout=1):
     return ((packed >> 4) | (packed << 4)).astype(np.uint8), sf
 
 
+def _nvfp4_with_scale(N, gs, layout, scale_of, code_divisor):
+    """NVFP4 built from a (possibly wrong) block-scale rule: scale_of(gs * amax / 6) gives the
+    stored E4M3 scale, code_divisor(stored, exact) the divisor of the codes."""
+    N = np.asarray(N, dtype=np.float64)
+    T, H = N.shape
+    gs = float(np.float32(gs))
+    blocks = N.reshape(T, H // 16, 16)
+    exact = gs * np.max(np.abs(blocks), axis=-1) / 6.0
+    sf = scale_of(exact)
+    div = code_divisor(sf, exact)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = _orig["round_to_format"](blocks * gs / div[..., None], R.E2M1)
+    q = np.where((sf == 0.0)[..., None], np.copysign(np.zeros_like(blocks), blocks), q)
+    c = R.encode_bits(q, R.E2M1).reshape(T, H)
+    packed = (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    t_i, b_i = np.meshgrid(np.arange(T), np.arange(H // 16), indexing="ij")
+    sfb = np.zeros(R.sf_size(T, H, layout), dtype=np.uint8)
+    sfb[R.sf_offset(t_i, b_i, H, layout)] = R.encode_bits(sf, R.E4M3)
+    return packed, sfb
+
+
+def _nvfp4_codes_from_unrounded_scale(N, gs, layout=1):
+    return _nvfp4_with_scale(N, gs, layout, lambda v: _orig["round_to_format"](v, R.E4M3),
+                             lambda sf, v: v)
+
+
+def _nvfp4_scale_truncated(N, gs, layout=1):
+    def rz(v):                      # the largest E4M3 value not above v (round toward zero)
+        g = R.decode_bits(np.arange(0x7F, dtype=np.uint8), R.E4M3)
+        return g[np.searchsorted(g, np.minimum(v, 448.0), side="right") - 1]
+    return _nvfp4_with_scale(N, gs, layout, rz, lambda sf, v: sf)
+
+
+def _nvfp4_zero_scale_unsigned(N, gs, layout=1):
+    packed, sfb = _orig["quant_nvfp4"](N, gs, layout)
+    T, H = np.asarray(N).shape
+    t_i, b_i = np.meshgrid(np.arange(T), np.arange(H // 16), indexing="ij")
+    zero = (sfb[R.sf_offset(t_i, b_i, H, layout)] == 0)            # [T, nb]
+    mask = np.repeat(zero, 8, axis=1)                                # 8 bytes per block
+    return np.where(mask, packed & 0x77, packed).astype(np.uint8), sfb
+
+
+def _fp8_without_saturation(N, s8):
+    codes = _orig["quant_fp8"](N, s8)
+    over = np.abs(np.asarray(N, np.float64) * float(np.float32(s8))) >= 464.0
+    return np.where(over, 0x7F, codes).astype(np.uint8)
+
+
+def _fp8_float32_product(N, s8):
+    p = (np.asarray(N, np.float64).astype(np.float32) * np.float32(s8)).astype(np.float64)
+    return _orig["quant_fp8"](p, 1.0)
+
+
 def _sf_offset_transposed(t, b, H, layout):
     if layout == R.SF_LINEAR:
         return _orig["sf_offset"](t, b, H, layout)
@@ -136,6 +189,12 @@ MUTANTS = [
                                              P.test_rmsnorm_constant_row_closed_form]),
     ("residual_rmsnorm", _rms_unrounded_input, [P.test_rmsnorm_correctly_rounded_bruteforce]),
     ("quant_nvfp4", _nvfp4_nibbles_swapped, [Q.test_nvfp4_exact_bruteforce]),
+    ("quant_nvfp4", _nvfp4_codes_from_unrounded_scale, [Q.test_nvfp4_exact_bruteforce,
+                                                        Q.test_nvfp4_exact_on_float32_near_ties]),
+    ("quant_nvfp4", _nvfp4_scale_truncated, [Q.test_nvfp4_exact_bruteforce]),
+    ("quant_nvfp4", _nvfp4_zero_scale_unsigned, [Q.test_nvfp4_zero_block_scale_gives_signed_zeros]),
+    ("quant_fp8", _fp8_without_saturation, [Q.test_fp8_exact_bruteforce_and_saturation]),
+    ("quant_fp8", _fp8_float32_product, [Q.test_fp8_exact_on_float32_near_ties]),
     ("sf_offset", _sf_offset_transposed, [Q.test_sf_layout_tile_structure]),
     ("sf_offset", _sf_offset_rows_in_order, [Q.test_sf_swizzled_map_matches_torch_to_blocked]),
     ("reference_unrounded", _ref_eps_outside, [P.test_reference_unrounded_and_magnitude_bruteforce]),

@@ -138,6 +138,70 @@ def test_fp8_exact_bruteforce_and_saturation():
     assert np.max(np.abs(O.decode_bits(codes, O.E4M3))) == 448.0
 
 
+def _bf16_values(lo, hi):
+    """Every positive bf16 value in [lo, hi]."""
+    a, b = (int(np.array([v], np.float32).view(np.uint32)[0] >> 16) for v in (lo, hi))
+    return (np.arange(a, b + 1, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_fp8_exact_on_float32_near_ties():
+    """Scales s8 = fl32(m / x0) put x0 * s8 within one float32 rounding of an E4M3 midpoint m
+    without equalling it (and x0 * 2^k on m * 2^k): the codes must follow the exact product,
+    which a rounding of the float32 product would get wrong on some of them."""
+    mids = [(a + b) / 2 for a, b in zip(*(lambda g: (g[:-1], g[1:]))(O.decode_bits(
+        np.arange(0x7F, dtype=np.uint8), O.E4M3)))]
+    x0s = _bf16_values(1.0, 1.96875)
+    n = 0
+    for i, x0 in enumerate(x0s):
+        m = mids[16 + (i * 13) % 80]
+        s8 = float(np.float32(m / x0))
+        xs = np.array([[x0 * 2.0 ** k for k in range(-5, 5)] + [-x0]])
+        codes = O.quant_fp8(xs, s8)
+        S = Fraction(s8)
+        for j, v in enumerate(xs[0]):
+            assert frac(O.decode_bits(codes[0, j], O.E4M3)) == rne_exact(frac(v) * S, "e4m3")
+            n += 1
+    assert n > 1000
+
+
+def test_nvfp4_exact_on_float32_near_ties():
+    """Global scales gs = fl32(m / x0) (block scale 1: block maximum 6 / gs) put x0 * gs / sf
+    within one float32 rounding of each E2M1 midpoint m; codes and scales against exact
+    rationals."""
+    n = 0
+    for i, x0 in enumerate(_bf16_values(1.0, 1.96875)[::2]):
+        m = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0][i % 7]
+        gs = float(np.float32(m / x0))
+        amax = float(O.round_to_format(np.array([6.0 / gs]), O.BF16)[0])
+        blk = np.zeros(16)
+        blk[0], blk[1], blk[2], blk[3] = amax, x0, -x0, x0 / 2
+        N = blk[None, :]
+        packed, sfb = O.quant_nvfp4(N, gs, O.SF_LINEAR)
+        codes = _unpack(packed)
+        G = Fraction(float(np.float32(gs)))
+        sf = rne_exact(G * frac(amax) / 6, "e4m3")
+        assert frac(O.decode_bits(np.uint8(sfb[0]), O.E4M3)) == sf
+        for j in range(16):
+            want = Fraction(0) if sf == 0 else rne_exact(frac(N[0, j]) * G / sf, "e2m1")
+            assert frac(O.decode_bits(np.uint8(codes[0, j]), O.E2M1)) == want
+            n += 1
+    assert n > 1000
+
+
+def test_nvfp4_zero_block_scale_gives_signed_zeros():
+    """A block whose gs * amax / 6 rounds to the E4M3 zero (below 2^-10) has scale byte 0 and,
+    by the reading of the pages' formula, zero codes that keep each element's sign (-0 too)."""
+    gs = 1.0
+    blk = np.array([3e-3, -3e-3, 1e-3, -1e-3, 0.0, -0.0, 5e-4, -5e-4] * 2)
+    assert float(np.max(np.abs(blk))) * gs / 6 < 2.0 ** -10
+    N = np.stack([blk, -blk])
+    packed, sfb = O.quant_nvfp4(N, gs, O.SF_LINEAR)
+    assert not sfb.any()
+    codes = _unpack(packed)
+    want = np.signbit(N).astype(np.uint8) << 3
+    assert np.array_equal(codes, want)
+
+
 def test_nonfinite_inputs_follow_the_stated_reading():
     """Non-finite values (the pages are silent): infinities saturate like any value above the
     largest finite code; a NaN gives the E4M3 NaN code S.1111.111 with S = 0 whatever its sign;
