@@ -92,3 +92,16 @@ def test_timing_plan_is_graph_replays_only(steps, warmup):
 def test_timing_plan_rejects_empty_runs():
     with pytest.raises(ValueError):
         bench.timing_plan(0, 5, 96)
+
+
+def test_more_than_one_gpu_is_refused():
+    """The path runs on one GPU: --gpus above 1 prints one JSON error line and exits with 2,
+    before touching any device."""
+    import json
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
